@@ -1,0 +1,223 @@
+/*
+ * attn_oracle.c -- fp64 CPU oracle for exact (non-causal) attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file, and everything else under oracle/,
+ * is the checker that the GPU path is compared against.  Only the tests,
+ * the smoke check and the CPU-baseline leg of the benchmark may load it.
+ * It shares no code, header, table or helper with the HIP library, and the
+ * HIP library never calls it.
+ *
+ * What it computes follows the page "GPU 内核与 FlashAttention" (hs-black,
+ * scaling-gpu-kernels), section 10 (standard attention: S = Q K^T, P = softmax(S),
+ * O = P V, with the usual 1/sqrt(d) factor on S) and section 11.1 (safe
+ * softmax: subtract the row maximum before exponentiating), and the
+ * log-sum-exp side output L = m + log(l) of sections 13.2 and 14.1.  The
+ * logit scale is an argument (the configurations use 1/sqrt(d)).  The page
+ * "Flash Attention实现深度解析" (maplevalley), section 3.1, fixes the packed
+ * variable-length layout [total, heads, d] with prefix offsets and an
+ * LSE of shape [batch, heads, max_seqlen].
+ *
+ * Everything is plain fp64: the caller decodes the 16-bit inputs exactly
+ * into double arrays.  Rows are independent; OpenMP spreads them over the
+ * host cores.  No blocking, fusion or reordering beyond the definition:
+ * for every query row the scores are formed, their maximum taken, the
+ * shifted exponentials summed, and the output is the normalised weighted
+ * sum of value rows.
+ *
+ * oracle_attention_online() is the second function: the one-pass blockwise
+ * recurrence of section 11.2 (two-block merge of (m, l)) and section 11.3
+ * (running unnormalised output rescaled by exp(m - m'), divided by l at the
+ * end), also in fp64.  It exists so that tests can show the recurrence the
+ * GPU kernel relies on reaches the same result as the definition.
+ */
+#include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Address of element [row, head, t] in a [rows, heads, d] (dense: [batch*n, heads, d]) array. */
+static inline int64_t at(int64_t row, int64_t head, int64_t t, int64_t heads, int64_t d) {
+  return (row * heads + head) * d + t;
+}
+
+/* One query row of the definition.  qrow0/krow0 are the first token rows of
+ * this sequence in the q and k/v arrays; i the query index in the sequence. */
+static void one_row(const double *q, const double *k, const double *v, double *o_row,
+                    double *lse_out, int64_t qrow0, int64_t krow0, int64_t i, int64_t nk,
+                    int64_t h, int64_t heads, int64_t d, double scale, double *s) {
+  /* s_j = scale * <q_i, k_j> */
+  for (int64_t j = 0; j < nk; ++j) {
+    double acc = 0.0;
+    for (int64_t t = 0; t < d; ++t)
+      acc += q[at(qrow0 + i, h, t, heads, d)] * k[at(krow0 + j, h, t, heads, d)];
+    s[j] = scale * acc;
+  }
+  /* m = max_j s_j */
+  double m = -INFINITY;
+  for (int64_t j = 0; j < nk; ++j) if (s[j] > m) m = s[j];
+  /* l = sum_j exp(s_j - m) */
+  double l = 0.0;
+  for (int64_t j = 0; j < nk; ++j) l += exp(s[j] - m);
+  /* O_i = sum_j (exp(s_j - m) / l) v_j */
+  for (int64_t t = 0; t < d; ++t) o_row[t] = 0.0;
+  for (int64_t j = 0; j < nk; ++j) {
+    double p = exp(s[j] - m) / l;
+    for (int64_t t = 0; t < d; ++t) o_row[t] += p * v[at(krow0 + j, h, t, heads, d)];
+  }
+  *lse_out = m + log(l);
+}
+
+/*
+ * Full attention.
+ *  q, o:   dense [batch, nq, heads, d]; varlen (cu != NULL) packed [cu[batch], heads, d]
+ *  k, v:   dense [batch, nk, heads, d]; varlen packed [cu[batch], heads, d]
+ *  lse:    [batch, heads, nq]  (varlen: nq is the row pitch, i.e. max length; rows past a
+ *          sequence's length are left untouched)
+ *  cu:     NULL for dense, else batch+1 non-decreasing prefix offsets shared by q and k.
+ * Returns 0, or -1 if scratch memory could not be obtained.
+ */
+int oracle_attention(const double *q, const double *k, const double *v, double *o, double *lse,
+                     int64_t batch, int64_t nq, int64_t nk, int64_t heads, int64_t d,
+                     double scale, const int64_t *cu) {
+  int64_t max_nk = nk;
+  if (cu) {
+    max_nk = 0;
+    for (int64_t b = 0; b < batch; ++b) if (cu[b + 1] - cu[b] > max_nk) max_nk = cu[b + 1] - cu[b];
+  }
+  int failed = 0;
+#pragma omp parallel
+  {
+    double *s = (double *)malloc(sizeof(double) * (size_t)(max_nk > 0 ? max_nk : 1));
+    if (!s) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for collapse(3) schedule(dynamic, 4)
+    for (int64_t b = 0; b < batch; ++b)
+      for (int64_t h = 0; h < heads; ++h)
+        for (int64_t i = 0; i < nq; ++i) {
+          if (!s) continue;
+          int64_t lq = cu ? cu[b + 1] - cu[b] : nq;
+          int64_t lk = cu ? cu[b + 1] - cu[b] : nk;
+          if (i >= lq || lk <= 0) continue;
+          int64_t qrow0 = cu ? cu[b] : b * nq;
+          int64_t krow0 = cu ? cu[b] : b * nk;
+          one_row(q, k, v, o + at(qrow0 + i, h, 0, heads, d), lse + (b * heads + h) * nq + i,
+                  qrow0, krow0, i, lk, h, heads, d, scale, s);
+        }
+    free(s);
+  }
+  return failed ? -1 : 0;
+}
+
+/*
+ * Selected rows only (for sampled checks at full size).  rows is n_rows triples
+ * (b, h, i); o_rows is [n_rows, d], lse_rows [n_rows].  Layout and cu as above.
+ */
+int oracle_attention_rows(const double *q, const double *k, const double *v, double *o_rows,
+                          double *lse_rows, int64_t batch, int64_t nq, int64_t nk, int64_t heads,
+                          int64_t d, double scale, const int64_t *cu, const int64_t *rows,
+                          int64_t n_rows) {
+  (void)batch;
+  int64_t max_nk = nk;
+  if (cu) {
+    max_nk = 0;
+    for (int64_t b = 0; b < batch; ++b) if (cu[b + 1] - cu[b] > max_nk) max_nk = cu[b + 1] - cu[b];
+  }
+  int failed = 0;
+#pragma omp parallel
+  {
+    double *s = (double *)malloc(sizeof(double) * (size_t)(max_nk > 0 ? max_nk : 1));
+    if (!s) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+      if (!s) continue;
+      int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+      int64_t lk = cu ? cu[b + 1] - cu[b] : nk;
+      int64_t qrow0 = cu ? cu[b] : b * nq;
+      int64_t krow0 = cu ? cu[b] : b * nk;
+      one_row(q, k, v, o_rows + r * d, lse_rows + r, qrow0, krow0, i, lk, h, heads, d, scale, s);
+    }
+    free(s);
+  }
+  return failed ? -1 : 0;
+}
+
+/*
+ * The blockwise one-pass recurrence (dense layout only), block = key-block size.
+ * State per query row: running max m (starts at -inf), running denominator l
+ * (starts at 0) and unnormalised output ot (starts at 0).  For each key block:
+ * m' = max(m, max of the block's scores); l <- exp(m - m') l + sum exp(s - m');
+ * ot <- exp(m - m') ot + sum exp(s - m') v; m <- m'.  At the end O = ot / l and
+ * LSE = m + log l.  exp(m - m') with m = -inf is taken as 0 (nothing accumulated yet).
+ */
+int oracle_attention_online(const double *q, const double *k, const double *v, double *o,
+                            double *lse, int64_t batch, int64_t nq, int64_t nk, int64_t heads,
+                            int64_t d, double scale, int64_t block) {
+  if (block <= 0) return -1;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double *s = (double *)malloc(sizeof(double) * (size_t)block);
+    double *ot = (double *)malloc(sizeof(double) * (size_t)(d > 0 ? d : 1));
+    if (!s || !ot) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for collapse(3) schedule(dynamic, 4)
+    for (int64_t b = 0; b < batch; ++b)
+      for (int64_t h = 0; h < heads; ++h)
+        for (int64_t i = 0; i < nq; ++i) {
+          if (!s || !ot) continue;
+          double m = -INFINITY, l = 0.0;
+          for (int64_t t = 0; t < d; ++t) ot[t] = 0.0;
+          for (int64_t j0 = 0; j0 < nk; j0 += block) {
+            int64_t nb = nk - j0 < block ? nk - j0 : block;
+            double mb = -INFINITY;
+            for (int64_t jj = 0; jj < nb; ++jj) {
+              double acc = 0.0;
+              for (int64_t t = 0; t < d; ++t)
+                acc += q[at(b * nq + i, h, t, heads, d)] * k[at(b * nk + j0 + jj, h, t, heads, d)];
+              s[jj] = scale * acc;
+              if (s[jj] > mb) mb = s[jj];
+            }
+            double mn = m > mb ? m : mb;
+            double alpha = (m == -INFINITY) ? 0.0 : exp(m - mn);
+            l *= alpha;
+            for (int64_t t = 0; t < d; ++t) ot[t] *= alpha;
+            for (int64_t jj = 0; jj < nb; ++jj) {
+              double p = exp(s[jj] - mn);
+              l += p;
+              for (int64_t t = 0; t < d; ++t) ot[t] += p * v[at(b * nk + j0 + jj, h, t, heads, d)];
+            }
+            m = mn;
+          }
+          for (int64_t t = 0; t < d; ++t) o[at(b * nq + i, h, t, heads, d)] = ot[t] / l;
+          lse[(b * heads + h) * nq + i] = m + log(l);
+        }
+    free(s);
+    free(ot);
+  }
+  return failed ? -1 : 0;
+}
+
+/* Number of OpenMP threads the oracle runs with (for reporting). */
+int oracle_num_threads(void) {
+  int n = 1;
+#pragma omp parallel
+  {
+#pragma omp single
+    {
+#ifdef _OPENMP
+      n = omp_get_num_threads();
+#endif
+    }
+  }
+  return n;
+}

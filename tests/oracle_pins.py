@@ -1,0 +1,217 @@
+"""Pins for the fp64 oracle: facts fixed by the pages and by mathematics, not by the
+oracle itself.  Each pin takes an oracle object (see oracle.Oracle) and raises
+AssertionError when the oracle disagrees.  test_oracle_pins.py runs them against the
+real oracle and against deliberately altered builds of it.
+
+Sources: page "GPU 内核与 FlashAttention" section 10 (attention as S = QK^T with a
+1/sqrt(d)-type scale, softmax, PV), section 11.1 (safe softmax), sections 11.2-11.3
+(the blockwise recurrence is exact), section 13.2 (LSE = m + log l).
+"""
+import json
+import math
+import os
+
+import numpy as np
+from scipy.special import logsumexp, softmax
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _one_head(x):
+    """[N, D] -> [1, N, 1, D]"""
+    x = np.asarray(x, dtype=np.float64)
+    return x.reshape(1, x.shape[0], 1, x.shape[1])
+
+
+def _rand(rng, *shape, std=1.0):
+    return rng.standard_normal(shape) * std
+
+
+def pin_hand_2x2(orc):
+    g = _golden("hand_cases.json")["hand_2x2"]
+    o, lse = orc.attention(_one_head(g["q"]), _one_head(g["k"]), _one_head(g["v"]), g["scale"])
+    e = math.e
+    closed_p = np.array([[e / (1 + e), 1 / (1 + e)], [1 / (1 + e), e / (1 + e)]])
+    closed_o = closed_p @ np.array(g["v"], dtype=np.float64)
+    np.testing.assert_allclose(o[0, :, 0, :], closed_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o[0, :, 0, :], np.array(g["O"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0], [math.log(1 + e)] * 2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0], g["LSE"], rtol=0, atol=1e-12)
+
+
+def pin_hand_4x4(orc):
+    g = _golden("hand_cases.json")["hand_4x4"]
+    o, lse = orc.attention(_one_head(g["q"]), _one_head(g["k"]), _one_head(g["v"]), g["scale"])
+    v = np.array(g["v"], dtype=np.float64)
+    for i, s in enumerate([0.5, 1.0, 1.5, 2.0]):
+        den = math.exp(s) + 3.0
+        p = np.full(4, 1.0 / den)
+        p[i] = math.exp(s) / den
+        np.testing.assert_allclose(o[0, i, 0, :], p @ v, rtol=0, atol=1e-12)
+        assert abs(lse[0, 0, i] - math.log(den)) < 1e-12
+    np.testing.assert_allclose(o[0, :, 0, :], np.array(g["O"]), rtol=0, atol=1e-9)
+    np.testing.assert_allclose(lse[0, 0], g["LSE"], rtol=0, atol=1e-12)
+
+
+def pin_values_one(orc):
+    """V = 1 everywhere: every output is a convex combination of ones, so O = 1."""
+    rng = np.random.default_rng(11)
+    q, k = _rand(rng, 2, 33, 3, 16), _rand(rng, 2, 47, 3, 16)
+    o, _ = orc.attention(q, k, np.ones_like(k), 0.25)
+    np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-12)
+
+
+def pin_identical_keys(orc):
+    """All keys equal: scores are constant along a row, so O_i = mean_j v_j and
+    LSE_i = s_i + ln Nk with s_i = scale <q_i, k>."""
+    rng = np.random.default_rng(12)
+    nk, d = 37, 8
+    q = _rand(rng, 1, 5, 2, d)
+    k = np.broadcast_to(_rand(rng, 1, 1, 2, d), (1, nk, 2, d)).copy()
+    v = _rand(rng, 1, nk, 2, d)
+    scale = 0.3
+    o, lse = orc.attention(q, k, v, scale)
+    for h in range(2):
+        mean_v = v[0, :, h, :].mean(axis=0)
+        for i in range(5):
+            np.testing.assert_allclose(o[0, i, h], mean_v, rtol=0, atol=1e-12)
+            s = scale * float(q[0, i, h] @ k[0, 0, h])
+            assert abs(lse[0, h, i] - (s + math.log(nk))) < 1e-12
+
+
+def pin_dominant_logit(orc):
+    """One key aligned with the query by a large factor: its weight is all but 1, so
+    O_i is that key's value row to within exp(-gap) * max|v|, and LSE_i is its score."""
+    rng = np.random.default_rng(13)
+    d, nk, jstar = 16, 20, 7
+    q = _rand(rng, 1, 1, 1, d)
+    k = _rand(rng, 1, nk, 1, d) * 0.1
+    k[0, jstar, 0] = 40.0 * q[0, 0, 0]
+    v = _rand(rng, 1, nk, 1, d)
+    o, lse = orc.attention(q, k, v, 1.0)
+    s = (k[0, :, 0] @ q[0, 0, 0])
+    gap = s[jstar] - np.max(np.delete(s, jstar))
+    assert gap > 40
+    bound = nk * math.exp(-gap) * np.abs(v).max() * 2
+    np.testing.assert_allclose(o[0, 0, 0], v[0, jstar, 0], rtol=0, atol=max(bound, 1e-12))
+    assert abs(lse[0, 0, 0] - s[jstar]) < max(nk * math.exp(-gap), 1e-12)
+
+
+def pin_value_identity_is_softmax(orc):
+    """Nk = d and V = I: row i of O is row i of P = softmax(scale q K^T), compared with
+    scipy's softmax and logsumexp on numpy's product (Nq != Nk, asymmetric Q and K)."""
+    rng = np.random.default_rng(14)
+    d = 24
+    q, k = _rand(rng, 1, 9, 1, d), _rand(rng, 1, d, 1, d)
+    v = np.eye(d).reshape(1, d, 1, d)
+    scale = 0.37
+    o, lse = orc.attention(q, k, v, scale)
+    s = scale * (q[0, :, 0, :] @ k[0, :, 0, :].T)
+    np.testing.assert_allclose(o[0, :, 0, :], softmax(s, axis=1), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse[0, 0], logsumexp(s, axis=1), rtol=0, atol=1e-12)
+
+
+def pin_single_key(orc):
+    """Nk = 1: the only weight is 1, O_i = v_0 and LSE_i = scale <q_i, k_0>."""
+    rng = np.random.default_rng(15)
+    q, k, v = _rand(rng, 2, 6, 2, 8), _rand(rng, 2, 1, 2, 8), _rand(rng, 2, 1, 2, 8)
+    o, lse = orc.attention(q, k, v, 0.7)
+    np.testing.assert_allclose(o, np.broadcast_to(v, o.shape), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, 0.7 * np.einsum("bihd,bhd->bhi", q, k[:, 0]), rtol=0, atol=1e-12)
+
+
+def pin_permutations_and_linearity(orc):
+    """Permuting keys with their values leaves O unchanged; permuting queries permutes
+    O's rows; O is linear in V."""
+    rng = np.random.default_rng(16)
+    q, k, v, v2 = (_rand(rng, 1, 11, 2, 8), _rand(rng, 1, 13, 2, 8), _rand(rng, 1, 13, 2, 8),
+                   _rand(rng, 1, 13, 2, 8))
+    o, lse = orc.attention(q, k, v, 0.5)
+    pk = rng.permutation(13)
+    o2, lse2 = orc.attention(q, k[:, pk], v[:, pk], 0.5)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse2, lse, rtol=0, atol=1e-12)
+    pq = rng.permutation(11)
+    o3, lse3 = orc.attention(q[:, pq], k, v, 0.5)
+    np.testing.assert_allclose(o3, o[:, pq], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse3, lse[:, :, pq], rtol=0, atol=1e-12)
+    oa, _ = orc.attention(q, k, v2, 0.5)
+    ob, _ = orc.attention(q, k, v + 2.0 * v2, 0.5)
+    np.testing.assert_allclose(ob, o + 2.0 * oa, rtol=0, atol=1e-12)
+
+
+def pin_shift_invariance(orc):
+    """Adding the same vector u to every key shifts row i's scores by scale <q_i, u>:
+    O is unchanged and LSE moves by exactly that amount."""
+    rng = np.random.default_rng(17)
+    q, k, v = _rand(rng, 1, 7, 1, 8), _rand(rng, 1, 19, 1, 8), _rand(rng, 1, 19, 1, 8)
+    u = _rand(rng, 8) * 3.0
+    o, lse = orc.attention(q, k, v, 0.4)
+    o2, lse2 = orc.attention(q, k + u, v, 0.4)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse2[0, 0] - lse[0, 0], 0.4 * (q[0, :, 0] @ u), rtol=0, atol=1e-11)
+
+
+def pin_large_logits(orc):
+    """Scores of several hundred (exp overflows fp64 past about 709): the max shift keeps
+    every value finite; compare with scipy on numpy's product."""
+    rng = np.random.default_rng(18)
+    q, k, v = _rand(rng, 1, 8, 1, 16, std=10.0), _rand(rng, 1, 30, 1, 16, std=10.0), _rand(rng, 1, 30, 1, 16)
+    o, lse = orc.attention(q, k, v, 2.0)
+    s = 2.0 * (q[0, :, 0] @ k[0, :, 0].T)
+    assert np.abs(s).max() > 750
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    np.testing.assert_allclose(o[0, :, 0], softmax(s, axis=1) @ v[0, :, 0], rtol=0, atol=1e-10)
+    np.testing.assert_allclose(lse[0, 0], logsumexp(s, axis=1), rtol=1e-14, atol=1e-10)
+
+
+def pin_online_recurrence_is_exact(orc):
+    """The blockwise recurrence (two-block merge of (m, l), running output rescaled by
+    exp(m - m')) reaches the direct result for any block size."""
+    rng = np.random.default_rng(19)
+    q, k, v = _rand(rng, 2, 10, 2, 8, std=2.0), _rand(rng, 2, 45, 2, 8, std=2.0), _rand(rng, 2, 45, 2, 8)
+    o, lse = orc.attention(q, k, v, 0.6)
+    for block in (1, 7, 16, 45, 64):
+        ob, lseb = orc.attention_online(q, k, v, 0.6, block)
+        np.testing.assert_allclose(ob, o, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lseb, lse, rtol=0, atol=1e-12)
+
+
+def pin_varlen_is_per_sequence(orc):
+    """Packed sequences attend only within themselves: each sequence's rows equal a
+    dense single-sequence call; LSE rows past a sequence's end are left untouched."""
+    rng = np.random.default_rng(20)
+    lens = [5, 1, 12, 8]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    total, h, d = int(cu[-1]), 2, 8
+    q, k, v = _rand(rng, total, h, d), _rand(rng, total, h, d), _rand(rng, total, h, d)
+    o, lse = orc.attention(q, k, v, 0.45, cu_seqlens=cu, max_seqlen=max(lens))
+    for b, L in enumerate(lens):
+        sl = slice(cu[b], cu[b + 1])
+        od, lsed = orc.attention(q[None, sl], k[None, sl], v[None, sl], 0.45)
+        np.testing.assert_allclose(o[sl], od[0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[b, :, :L], lsed[0], rtol=0, atol=1e-12)
+        assert np.all(np.isnan(lse[b, :, L:]))
+
+
+def pin_rows_match_full(orc):
+    """The selected-rows entry point returns the same rows as the full one."""
+    rng = np.random.default_rng(21)
+    q, k, v = _rand(rng, 2, 9, 3, 8), _rand(rng, 2, 14, 3, 8), _rand(rng, 2, 14, 3, 8)
+    o, lse = orc.attention(q, k, v, 0.5)
+    rows = [(0, 0, 0), (1, 2, 8), (0, 1, 4), (1, 0, 3)]
+    orow, lrow = orc.attention_rows(q, k, v, 0.5, rows)
+    for n, (b, h, i) in enumerate(rows):
+        np.testing.assert_allclose(orow[n], o[b, i, h], rtol=0, atol=1e-14)
+        assert abs(lrow[n] - lse[b, h, i]) < 1e-14
+
+
+PINS = [pin_hand_2x2, pin_hand_4x4, pin_values_one, pin_identical_keys, pin_dominant_logit,
+        pin_value_identity_is_softmax, pin_single_key, pin_permutations_and_linearity,
+        pin_shift_invariance, pin_large_logits, pin_online_recurrence_is_exact,
+        pin_varlen_is_per_sequence, pin_rows_match_full]

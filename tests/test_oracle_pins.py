@@ -1,0 +1,78 @@
+"""The fp64 oracle checked against what the pages and mathematics fix (CPU only)."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle_pins import PINS
+from exact_attention_17_amd import metrics
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin, oracle_mod):
+    pin(oracle_mod.Oracle())
+
+
+# Plausible mistakes, planted in copies of the oracle source compiled on the CPU.
+MUTATIONS = {
+    "scale_dropped": ("s[j] = scale * acc;", "s[j] = acc;"),
+    "exp_sign_flipped": ("l += exp(s[j] - m);", "l += exp(m - s[j]);"),
+    "scores_wrong_index": ("acc += q[at(qrow0 + i, h, t, heads, d)] * k[at(krow0 + j, h, t, heads, d)];",
+                          "acc += q[at(qrow0 + (j % (nk < 1 ? 1 : nk)) % (i + 1), h, t, heads, d)]"
+                          " * k[at(krow0 + (i % nk), h, t, heads, d)];"),
+    "no_normalisation": ("double p = exp(s[j] - m) / l;", "double p = exp(s[j] - m);"),
+    "lse_without_max": ("*lse_out = m + log(l);", "*lse_out = log(l);"),
+    "no_max_shift": ("l += exp(s[j] - m);", "l += exp(s[j]);"),
+    "value_row_of_query": ("o_row[t] += p * v[at(krow0 + j, h, t, heads, d)];",
+                           "o_row[t] += p * v[at(krow0 + (i % nk), h, t, heads, d)];"),
+    "max_is_min": ("if (s[j] > m) m = s[j];", "if (m == -INFINITY || s[j] < m) m = s[j];"),
+    "online_no_rescale": ("for (int64_t t = 0; t < d; ++t) ot[t] *= alpha;", ""),
+    "varlen_ignores_offsets": ("int64_t krow0 = cu ? cu[b] : b * nk;\n          one_row(",
+                               "int64_t krow0 = cu ? 0 : b * nk;\n          one_row("),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, oracle_mod, tmp_path):
+    old, new = MUTATIONS[name]
+    src = oracle_mod.source_text()
+    assert src.count(old) >= 1, "mutation anchor not found: " + name
+    lib = oracle_mod.compile_source(src.replace(old, new), str(tmp_path / ("m_%s.so" % name)))
+    orc = oracle_mod.Oracle(lib)
+    caught = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(orc)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, "no pin caught the planted mistake " + name
+
+
+def test_slice_accounting_matches_page():
+    g = json.load(open(os.path.join(HERE, "golden", "slice_accounting.json")))
+    nq, nk, d = g["seqlen_q"], g["seqlen_k"], g["d_head"]
+    fl = metrics.slice_page_flops(nq, nk, d)
+    assert abs(fl / g["page_flops_approx"] - 1) <= g["page_flops_rel_tol"]
+    by = metrics.fwd_bytes(1, 1, nq, nk, d, g["elt_bytes"], with_lse=False)
+    assert abs(by / g["page_gmem_bytes_approx"] - 1) <= g["page_gmem_bytes_rel_tol"]
+    inten = metrics.intensity(metrics.fwd_flops(1, 1, nq, nk, d), by)
+    assert abs(inten / g["page_intensity_approx"] - 1) <= g["page_intensity_rel_tol"]
+
+
+def test_standard_attention_io_matches_page():
+    g = json.load(open(os.path.join(HERE, "golden", "standard_attention_io.json")))
+    n, d = g["n"], g["d"]
+    assert abs(metrics.standard_attention_hbm_elements(n, d) / g["standard_elements_approx"] - 1) \
+        <= g["standard_elements_rel_tol"]
+    assert abs(n * n / g["s_elements_approx"] - 1) <= g["s_elements_rel_tol"]
+    assert abs(2 * n * n / g["s_bytes_bf16_approx"] - 1) <= g["s_bytes_rel_tol"]
+    kv = metrics.fwd_bytes(1, 1, 0, n, d, with_lse=False)
+    assert kv == g["kv_one_head_bytes_approx"]
+
+
+def test_full_workload_flops_is_2_pow_41():
+    assert metrics.fwd_flops(16, 16, 4096, 4096, 128) == 2 ** 41
