@@ -1,0 +1,58 @@
+"""Build libfa_fwd.so (the HIP kernels and the C ABI) in-tree with hipcc for gfx950.
+
+    python -m exact_attention_17_amd.build
+
+Every HIP source is compiled with packed-fp32 instructions disabled
+(-Xclang -target-feature -Xclang -packed-fp32-ops).
+"""
+import concurrent.futures
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libfa_fwd.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+def sources():
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
+
+
+def _compile(src, extra):
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = [HIPCC] + FLAGS + extra + ["-c", src, "-o", obj]
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(ln for ln in p.stdout.splitlines() if "is not a recognized feature" not in ln)
+    if p.returncode != 0:
+        raise RuntimeError("hipcc failed on %s:\n%s" % (src, out))
+    return obj, out
+
+
+def build(jobs=None, extra=(), verbose=False):
+    """Compile every source under csrc/ and link libfa_fwd.so.  Returns the library path."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = jobs or min(8, os.cpu_count() or 4)
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(lambda s: _compile(s, list(extra)), sources()))
+    if verbose:
+        for obj, out in results:
+            if out.strip():
+                print(out)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
+    subprocess.check_call(cmd)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,317 @@
+// fa_fwd_api.cpp -- the C ABI declared in include/fa_fwd.h: argument checks, the registry
+// of compiled tile configurations, configuration choice, launch, and the autotuner.
+//
+// Argument checks run on the host before any HIP call, so a rejected call touches
+// neither the device nor the runtime.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "fa_fwd.h"
+#include "fa_internal.h"
+
+namespace {
+
+using fa::FaArgs;
+using fa::KernelEntry;
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string &msg) {
+  g_last_error = msg;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return FA_OK;
+}
+
+// ---------------------------------------------------------------- registry
+std::vector<KernelEntry> *g_entries = nullptr;
+
+void add_entry(const KernelEntry &e) { g_entries->push_back(e); }
+
+const std::vector<KernelEntry> &entries() {
+  static std::once_flag once;
+  std::call_once(once, [] {
+    g_entries = new std::vector<KernelEntry>();
+    fa::register_bf16_d32(add_entry);
+    fa::register_bf16_d64(add_entry);
+    fa::register_bf16_d128(add_entry);
+    fa::register_fp16_d32(add_entry);
+    fa::register_fp16_d64(add_entry);
+    fa::register_fp16_d128(add_entry);
+  });
+  return *g_entries;
+}
+
+const KernelEntry *find_entry(int dtype, int d, const fa_tile_config_t &c) {
+  for (const auto &e : entries())
+    if (e.dtype == dtype && e.d_head == d && e.br == c.br && e.bc == c.bc && e.waves == c.waves &&
+        e.stages == c.stages)
+      return &e;
+  return nullptr;
+}
+
+fa_tile_config_t cfg_of(const KernelEntry &e) { return fa_tile_config_t{e.br, e.bc, e.waves, e.stages}; }
+
+bool valid_dtype(int dtype) { return dtype == FA_BF16 || dtype == FA_FP16; }
+bool valid_d(int d) { return d == 32 || d == 64 || d == 128; }
+
+// ------------------------------------------------------ configuration choice
+std::mutex g_cfg_mu;
+std::map<std::pair<int, int>, fa_tile_config_t> g_forced;  // (d, dtype) -> config
+// (d, dtype, varlen, ceil(log2(seqlen_q))) -> tuned config
+std::map<std::tuple<int, int, int, int>, fa_tile_config_t> g_tuned;
+
+int log2_bucket(int n) {
+  int b = 0;
+  while ((1LL << b) < n) ++b;
+  return b;
+}
+
+fa_tile_config_t default_config(int seqlen_q, int d) {
+  (void)d;
+  // A single short query tile gains nothing from 4 wavefronts.
+  if (seqlen_q <= 64) return fa_tile_config_t{64, 64, 2, 2};
+  return fa_tile_config_t{128, 64, 4, 2};
+}
+
+fa_tile_config_t choose_config(int seqlen_q, int d, int dtype, bool varlen) {
+  std::lock_guard<std::mutex> lk(g_cfg_mu);
+  auto f = g_forced.find({d, dtype});
+  if (f != g_forced.end()) return f->second;
+  auto t = g_tuned.find({d, dtype, varlen ? 1 : 0, log2_bucket(seqlen_q)});
+  if (t != g_tuned.end()) return t->second;
+  return default_config(seqlen_q, d);
+}
+
+// ------------------------------------------------------------ arg checks
+int check_args(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
+               int seqlen_q, int seqlen_k, int n_heads, int d_head, float scale,
+               const int32_t *cu_seqlens, int dtype) {
+  if (!q || !k || !v || !o || !lse)
+    return fail(FA_ERR_INVALID_ARG, "q, k, v, o and lse must be non-null device pointers");
+  if (!valid_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "dtype must be FA_BF16 (0) or FA_FP16 (1)");
+  if (batch < 1 || n_heads < 1 || seqlen_q < 1 || seqlen_k < 1)
+    return fail(FA_ERR_INVALID_ARG, "batch, n_heads, seqlen_q and seqlen_k must be >= 1");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (!valid_d(d_head)) return fail(FA_ERR_UNSUPPORTED, "d_head must be 32, 64 or 128");
+  if (cu_seqlens && seqlen_q != seqlen_k)
+    return fail(FA_ERR_INVALID_ARG, "with cu_seqlens, seqlen_q and seqlen_k must both be the max length");
+  auto mis = [](const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; };
+  if (mis(q, 16) || mis(k, 16) || mis(v, 16) || mis(o, 16))
+    return fail(FA_ERR_MISALIGNED, "q, k, v and o must be 16-byte aligned");
+  if (mis(lse, 4)) return fail(FA_ERR_MISALIGNED, "lse must be 4-byte aligned");
+  // Per-sequence byte offsets are 32-bit in the kernel (buffer addressing); one tile of
+  // slack past the longest sequence.
+  const int64_t row_bytes = (int64_t)n_heads * d_head * 2;
+  const int64_t longest = std::max(seqlen_q, seqlen_k);
+  if ((longest + 256) * row_bytes >= (int64_t)INT32_MAX)
+    return fail(FA_ERR_UNSUPPORTED, "sequence length x n_heads x d_head too large for 32-bit offsets");
+  const int64_t wgs = (int64_t)batch * n_heads * ((seqlen_q + 63) / 64);
+  if (wgs >= (int64_t)INT32_MAX) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  return FA_OK;
+}
+
+FaArgs make_args(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
+                 int seqlen_q, int seqlen_k, int n_heads, float scale, const int32_t *cu_seqlens,
+                 int br) {
+  FaArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.cu_seqlens = cu_seqlens;
+  a.batch = batch;
+  a.seqlen_q = seqlen_q;
+  a.seqlen_k = seqlen_k;
+  a.heads = n_heads;
+  a.n_qtiles = (seqlen_q + br - 1) / br;
+  a.total_wgs = batch * n_heads * a.n_qtiles;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
+  return a;
+}
+
+int launch_entry(const KernelEntry &e, const void *q, const void *k, const void *v, void *o,
+                 float *lse, int batch, int seqlen_q, int seqlen_k, int n_heads, float scale,
+                 const int32_t *cu_seqlens, void *stream) {
+  const FaArgs a = make_args(q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, scale, cu_seqlens, e.br);
+  hipError_t err = e.launch(a, reinterpret_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(err));
+  return ok();
+}
+
+constexpr int kLdsLimit = 160 * 1024;
+
+int lds_bytes_of(int d, const fa_tile_config_t &c) { return c.stages * 2 * c.bc * d * 2; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int seqlen_q,
+           int seqlen_k, int n_heads, int d_head, float scale, const int32_t *cu_seqlens, int dtype,
+           void *stream) {
+  int st = check_args(q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, d_head, scale, cu_seqlens, dtype);
+  if (st != FA_OK) return st;
+  const fa_tile_config_t c = choose_config(seqlen_q, d_head, dtype, cu_seqlens != nullptr);
+  const KernelEntry *e = find_entry(dtype, d_head, c);
+  if (!e) return fail(FA_ERR_UNSUPPORTED, "no compiled kernel for the chosen tile configuration");
+  return launch_entry(*e, q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, scale, cu_seqlens, stream);
+}
+
+int fa_fwd_set_config(int d_head, int dtype, const fa_tile_config_t *cfg) {
+  if (!valid_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "dtype must be FA_BF16 (0) or FA_FP16 (1)");
+  if (!valid_d(d_head)) return fail(FA_ERR_UNSUPPORTED, "d_head must be 32, 64 or 128");
+  std::lock_guard<std::mutex> lk(g_cfg_mu);
+  if (!cfg) {
+    g_forced.erase({d_head, dtype});
+    return ok();
+  }
+  if (!find_entry(dtype, d_head, *cfg))
+    return fail(FA_ERR_UNSUPPORTED, "no compiled kernel for this tile configuration");
+  g_forced[{d_head, dtype}] = *cfg;
+  return ok();
+}
+
+int fa_fwd_get_config(int batch, int seqlen_q, int seqlen_k, int n_heads, int d_head, int dtype,
+                      int varlen, fa_tile_config_t *out) {
+  if (!out) return fail(FA_ERR_INVALID_ARG, "out must be non-null");
+  if (!valid_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "dtype must be FA_BF16 (0) or FA_FP16 (1)");
+  if (batch < 1 || n_heads < 1 || seqlen_q < 1 || seqlen_k < 1)
+    return fail(FA_ERR_INVALID_ARG, "batch, n_heads, seqlen_q and seqlen_k must be >= 1");
+  if (!valid_d(d_head)) return fail(FA_ERR_UNSUPPORTED, "d_head must be 32, 64 or 128");
+  *out = choose_config(seqlen_q, d_head, dtype, varlen != 0);
+  return ok();
+}
+
+int fa_fwd_num_configs(int d_head, int dtype) {
+  if (!valid_dtype(dtype)) return fail(-FA_ERR_INVALID_ARG, "dtype must be FA_BF16 (0) or FA_FP16 (1)");
+  if (!valid_d(d_head)) return fail(-FA_ERR_UNSUPPORTED, "d_head must be 32, 64 or 128");
+  int n = 0;
+  for (const auto &e : entries()) n += (e.dtype == dtype && e.d_head == d_head);
+  ok();
+  return n;
+}
+
+int fa_fwd_list_configs(int d_head, int dtype, fa_tile_config_t *out, int capacity) {
+  if (!valid_dtype(dtype)) return fail(-FA_ERR_INVALID_ARG, "dtype must be FA_BF16 (0) or FA_FP16 (1)");
+  if (!valid_d(d_head)) return fail(-FA_ERR_UNSUPPORTED, "d_head must be 32, 64 or 128");
+  if (capacity < 0 || (capacity > 0 && !out)) return fail(-FA_ERR_INVALID_ARG, "bad output buffer");
+  int n = 0;
+  for (const auto &e : entries()) {
+    if (e.dtype != dtype || e.d_head != d_head) continue;
+    if (n < capacity) out[n] = cfg_of(e);
+    ++n;
+  }
+  ok();
+  return n;
+}
+
+int fa_fwd_config_lds_bytes(int d_head, const fa_tile_config_t *cfg) {
+  if (!cfg) return fail(-FA_ERR_INVALID_ARG, "cfg must be non-null");
+  if (!valid_d(d_head)) return fail(-FA_ERR_UNSUPPORTED, "d_head must be 32, 64 or 128");
+  if (cfg->bc < 1 || cfg->stages < 1) return fail(-FA_ERR_INVALID_ARG, "bc and stages must be >= 1");
+  ok();
+  return lds_bytes_of(d_head, *cfg);
+}
+
+int fa_fwd_config_resources(int d_head, int dtype, const fa_tile_config_t *cfg, int *vgprs,
+                            int *spill_bytes, int *lds_bytes) {
+  if (!cfg) return fail(FA_ERR_INVALID_ARG, "cfg must be non-null");
+  if (!valid_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "dtype must be FA_BF16 (0) or FA_FP16 (1)");
+  if (!valid_d(d_head)) return fail(FA_ERR_UNSUPPORTED, "d_head must be 32, 64 or 128");
+  const KernelEntry *e = find_entry(dtype, d_head, *cfg);
+  if (!e) return fail(FA_ERR_UNSUPPORTED, "no compiled kernel for this tile configuration");
+  hipFuncAttributes attr;
+  hipError_t err = hipFuncGetAttributes(&attr, e->kernel);
+  if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("hipFuncGetAttributes: ") + hipGetErrorString(err));
+  if (vgprs) *vgprs = attr.numRegs;
+  if (spill_bytes) *spill_bytes = (int)attr.localSizeBytes;
+  if (lds_bytes) *lds_bytes = (int)attr.sharedSizeBytes;
+  return ok();
+}
+
+int fa_fwd_autotune(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
+                    int seqlen_q, int seqlen_k, int n_heads, int d_head, float scale,
+                    const int32_t *cu_seqlens, int dtype, void *stream, int reps,
+                    fa_tile_config_t *chosen, float *best_ms) {
+  int st = check_args(q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, d_head, scale, cu_seqlens, dtype);
+  if (st != FA_OK) return st;
+  if (reps < 1) return fail(FA_ERR_INVALID_ARG, "reps must be >= 1");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  auto cleanup = [&] {
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+  };
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    cleanup();
+    return fail(FA_ERR_HIP, "hipEventCreate failed");
+  }
+  const KernelEntry *best = nullptr;
+  float best_t = 0.f;
+  for (const auto &e : entries()) {
+    if (e.dtype != dtype || e.d_head != d_head) continue;
+    const fa_tile_config_t c = cfg_of(e);
+    if (lds_bytes_of(d_head, c) > kLdsLimit) continue;  // does not fit one CU's LDS
+    hipFuncAttributes attr;
+    if (hipFuncGetAttributes(&attr, e.kernel) != hipSuccess) continue;
+    if (attr.localSizeBytes > 0) continue;  // spills registers
+    int rc = launch_entry(e, q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, scale, cu_seqlens, stream);
+    if (rc != FA_OK) {
+      cleanup();
+      return rc;
+    }
+    if (hipEventRecord(e0, s) != hipSuccess) break;
+    for (int r = 0; r < reps; ++r)
+      (void)launch_entry(e, q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, scale, cu_seqlens, stream);
+    if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) {
+      cleanup();
+      return fail(FA_ERR_HIP, "event timing failed");
+    }
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+      cleanup();
+      return fail(FA_ERR_HIP, "hipEventElapsedTime failed");
+    }
+    ms /= reps;
+    if (!best || ms < best_t) {
+      best = &e;
+      best_t = ms;
+    }
+  }
+  cleanup();
+  if (!best) return fail(FA_ERR_UNSUPPORTED, "no configuration passed the LDS / spill filter");
+  {
+    std::lock_guard<std::mutex> lk(g_cfg_mu);
+    g_tuned[{d_head, dtype, cu_seqlens ? 1 : 0, log2_bucket(seqlen_q)}] = cfg_of(*best);
+  }
+  // Leave O and LSE holding the winner's result.
+  int rc = launch_entry(*best, q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, scale, cu_seqlens, stream);
+  if (rc != FA_OK) return rc;
+  if (hipStreamSynchronize(s) != hipSuccess) return fail(FA_ERR_HIP, "hipStreamSynchronize failed");
+  if (chosen) *chosen = cfg_of(*best);
+  if (best_ms) *best_ms = best_t;
+  return ok();
+}
+
+const char *fa_last_error(void) { return g_last_error.c_str(); }
+
+const char *fa_version(void) { return "fa_fwd 0.1 (gfx950)"; }
+
+}  // extern "C"

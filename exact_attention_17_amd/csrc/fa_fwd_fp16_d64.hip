@@ -1,0 +1,16 @@
+// Compiled tile configurations for fp16, d_head = 64 (the tuner's search space; page
+// "Flash Attention 2 Chapter6", Kernel 7: B_r x B_c x waves, plus the K/V buffering depth).
+#include "fa_fwd_kernel.h"
+
+namespace fa {
+
+void register_fp16_d64(void (*add)(const KernelEntry &)) {
+  add(make_entry<64, 128, 64, 4, 2, true>());
+  add(make_entry<64, 128, 32, 4, 2, true>());
+  add(make_entry<64, 128, 128, 4, 2, true>());
+  add(make_entry<64, 64, 64, 2, 2, true>());
+  add(make_entry<64, 256, 64, 8, 2, true>());
+  add(make_entry<64, 128, 64, 4, 1, true>());
+}
+
+}  // namespace fa

@@ -1,0 +1,223 @@
+"""Thin ctypes binding over libfa_fwd.so (include/fa_fwd.h).
+
+Argument marshalling only: every step of the forward pass runs in the library's
+HIP kernels.  PyTorch supplies device memory and the current stream.  If the
+library is missing this module raises; there is no fallback.
+"""
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfa_fwd.so")
+
+FA_BF16, FA_FP16 = 0, 1
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_MISALIGNED, FA_ERR_HIP = 0, 1, 2, 3, 4
+
+# Every exported symbol of include/fa_fwd.h.
+EXPORTS = ("fa_fwd", "fa_fwd_autotune", "fa_fwd_set_config", "fa_fwd_get_config",
+           "fa_fwd_num_configs", "fa_fwd_list_configs", "fa_fwd_config_lds_bytes",
+           "fa_fwd_config_resources", "fa_last_error", "fa_version")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("fa_fwd status %d: %s" % (status, msg))
+        self.status = status
+
+
+class TileConfig(ctypes.Structure):
+    _fields_ = [("br", ctypes.c_int), ("bc", ctypes.c_int), ("waves", ctypes.c_int),
+                ("stages", ctypes.c_int)]
+
+    def as_tuple(self):
+        return (self.br, self.bc, self.waves, self.stages)
+
+    def __repr__(self):
+        return "TileConfig(br=%d, bc=%d, waves=%d, stages=%d)" % self.as_tuple()
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+
+
+def lib():
+    """Load libfa_fwd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        # torch ships its own HIP runtime (same soname as the system one).  Load it first so
+        # that libfa_fwd.so binds to that runtime: two HIP runtimes in one process do not
+        # share devices, memory or streams.
+        import torch  # noqa: F401
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libfa_fwd.so is not built: run `python -m exact_attention_17_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.fa_fwd.restype = _i
+        L.fa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.c_float, _vp, _i, _vp]
+        L.fa_fwd_autotune.restype = _i
+        L.fa_fwd_autotune.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.c_float, _vp,
+                                      _i, _vp, _i, ctypes.POINTER(TileConfig),
+                                      ctypes.POINTER(ctypes.c_float)]
+        L.fa_fwd_set_config.restype = _i
+        L.fa_fwd_set_config.argtypes = [_i, _i, ctypes.POINTER(TileConfig)]
+        L.fa_fwd_get_config.restype = _i
+        L.fa_fwd_get_config.argtypes = [_i, _i, _i, _i, _i, _i, _i, ctypes.POINTER(TileConfig)]
+        L.fa_fwd_num_configs.restype = _i
+        L.fa_fwd_num_configs.argtypes = [_i, _i]
+        L.fa_fwd_list_configs.restype = _i
+        L.fa_fwd_list_configs.argtypes = [_i, _i, ctypes.POINTER(TileConfig), _i]
+        L.fa_fwd_config_lds_bytes.restype = _i
+        L.fa_fwd_config_lds_bytes.argtypes = [_i, ctypes.POINTER(TileConfig)]
+        L.fa_fwd_config_resources.restype = _i
+        L.fa_fwd_config_resources.argtypes = [_i, _i, ctypes.POINTER(TileConfig),
+                                              ctypes.POINTER(_i), ctypes.POINTER(_i), ctypes.POINTER(_i)]
+        L.fa_last_error.restype = ctypes.c_char_p
+        L.fa_last_error.argtypes = []
+        L.fa_version.restype = ctypes.c_char_p
+        L.fa_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def fa_last_error():
+    return lib().fa_last_error().decode()
+
+
+def fa_version():
+    return lib().fa_version().decode()
+
+
+def _check(status):
+    if status != FA_OK:
+        raise FaError(status, fa_last_error())
+    return status
+
+
+def fa_fwd_raw(q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, d_head, scale, cu_seqlens,
+               dtype, stream):
+    """The C call with integer pointers; returns the status code (no exception)."""
+    return lib().fa_fwd(q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, d_head, float(scale),
+                        cu_seqlens, dtype, stream)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float16:
+        return FA_FP16
+    raise TypeError("q, k, v must be bfloat16 or float16")
+
+
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def _shape_args(q, k, v, cu_seqlens, max_seqlen):
+    if cu_seqlens is None:
+        if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+            raise ValueError("dense q, k, v must be [B, N, H, D] with k and v alike")
+        batch, nq, heads, d = q.shape
+        if k.shape[0] != batch or k.shape[2] != heads or k.shape[3] != d:
+            raise ValueError("q and k disagree on batch, heads or d_head")
+        return batch, nq, k.shape[1], heads, d
+    if q.dim() != 3 or q.shape != k.shape or k.shape != v.shape:
+        raise ValueError("varlen q, k, v must all be [total, H, D]")
+    if max_seqlen is None:
+        raise ValueError("varlen calls need max_seqlen")
+    return cu_seqlens.numel() - 1, int(max_seqlen), int(max_seqlen), q.shape[1], q.shape[2]
+
+
+def fa_fwd(q, k, v, o=None, lse=None, scale=None, cu_seqlens=None, max_seqlen=None, stream=None):
+    """Attention forward on torch device tensors; returns (o, lse).
+
+    Dense: q [B, Nq, H, D], k/v [B, Nk, H, D] -> o like q, lse [B, H, Nq] fp32.
+    Varlen: q/k/v [total, H, D], cu_seqlens int32 [B+1] on the device, max_seqlen ->
+    o like q, lse [B, H, max_seqlen] (rows past a sequence's end untouched).
+    o and lse may be given (preallocated); otherwise they are allocated with torch.
+    """
+    import torch
+    batch, nq, nk, heads, d = _shape_args(q, k, v, cu_seqlens, max_seqlen)
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
+        raise TypeError("cu_seqlens must be an int32 device tensor")
+    if scale is None:
+        scale = d ** -0.5
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((batch, heads, nq), dtype=torch.float32, device=q.device)
+    st = lib().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), batch, nq,
+                      nk, heads, d, float(scale), cu_seqlens.data_ptr() if cu_seqlens is not None else None,
+                      _dtype_code(q), _stream_handle(stream, q.device))
+    _check(st)
+    return o, lse
+
+
+def fa_fwd_autotune(q, k, v, o, lse, scale=None, cu_seqlens=None, max_seqlen=None, reps=5, stream=None):
+    """Time every admissible compiled configuration on these buffers; returns (TileConfig, ms)."""
+    batch, nq, nk, heads, d = _shape_args(q, k, v, cu_seqlens, max_seqlen)
+    if scale is None:
+        scale = d ** -0.5
+    chosen = TileConfig()
+    ms = ctypes.c_float()
+    st = lib().fa_fwd_autotune(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                               batch, nq, nk, heads, d, float(scale),
+                               cu_seqlens.data_ptr() if cu_seqlens is not None else None,
+                               _dtype_code(q), _stream_handle(stream, q.device), int(reps),
+                               ctypes.byref(chosen), ctypes.byref(ms))
+    _check(st)
+    return chosen, ms.value
+
+
+def fa_fwd_set_config(d_head, dtype, cfg):
+    """Force (br, bc, waves, stages) for (d_head, dtype); cfg None = automatic."""
+    if cfg is None:
+        return _check(lib().fa_fwd_set_config(d_head, dtype, None))
+    c = cfg if isinstance(cfg, TileConfig) else TileConfig(*cfg)
+    return _check(lib().fa_fwd_set_config(d_head, dtype, ctypes.byref(c)))
+
+
+def fa_fwd_get_config(batch, seqlen_q, seqlen_k, n_heads, d_head, dtype, varlen=False):
+    c = TileConfig()
+    _check(lib().fa_fwd_get_config(batch, seqlen_q, seqlen_k, n_heads, d_head, dtype, int(bool(varlen)),
+                                   ctypes.byref(c)))
+    return c
+
+
+def fa_fwd_num_configs(d_head, dtype):
+    n = lib().fa_fwd_num_configs(d_head, dtype)
+    if n < 0:
+        raise FaError(-n, fa_last_error())
+    return n
+
+
+def fa_fwd_list_configs(d_head, dtype):
+    n = fa_fwd_num_configs(d_head, dtype)
+    arr = (TileConfig * max(n, 1))()
+    lib().fa_fwd_list_configs(d_head, dtype, arr, n)
+    return [arr[i] for i in range(n)]
+
+
+def fa_fwd_config_lds_bytes(d_head, cfg):
+    c = cfg if isinstance(cfg, TileConfig) else TileConfig(*cfg)
+    n = lib().fa_fwd_config_lds_bytes(d_head, ctypes.byref(c))
+    if n < 0:
+        raise FaError(-n, fa_last_error())
+    return n
+
+
+def fa_fwd_config_resources(d_head, dtype, cfg):
+    """(vgprs, spill_bytes, lds_bytes) of a compiled configuration (needs a GPU)."""
+    c = cfg if isinstance(cfg, TileConfig) else TileConfig(*cfg)
+    a, b, l_ = _i(), _i(), _i()
+    _check(lib().fa_fwd_config_resources(d_head, dtype, ctypes.byref(c), ctypes.byref(a), ctypes.byref(b),
+                                         ctypes.byref(l_)))
+    return a.value, b.value, l_.value

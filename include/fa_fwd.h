@@ -1,0 +1,138 @@
+/*
+ * fa_fwd.h -- C ABI of an exact-attention forward pass (FlashAttention-2
+ * style) for AMD MI355X (gfx950).
+ *
+ * Operation (page "GPU 内核与 FlashAttention", sections 10, 11 and 14; the
+ * kernel interface of "Flash Attention实现深度解析", section 3.1):
+ *
+ *   for every batch entry b, head h and query row i:
+ *     s_ij   = scale * <q[b,i,h,:], k[b,j,h,:]>          (j over the keys)
+ *     O[b,i,h,:] = sum_j softmax_j(s_i.) * v[b,j,h,:]
+ *     LSE[b,h,i] = log sum_j exp(s_ij)                    (natural log)
+ *
+ * computed tile by tile with the online softmax, never forming the Nq x Nk
+ * score matrix.  Inputs and O are 16-bit (bf16 or fp16, the same type for
+ * all four); the softmax and all accumulation are fp32; LSE is fp32.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *    library allocates no device memory in fa_fwd and keeps no pointer after
+ *    a call returns.
+ *  - Dense layout (cu_seqlens == NULL):
+ *      q, o : [batch, seqlen_q, n_heads, d_head], contiguous
+ *      k, v : [batch, seqlen_k, n_heads, d_head], contiguous
+ *      lse  : [batch, n_heads, seqlen_q] fp32
+ *  - Packed variable-length layout (cu_seqlens != NULL), self-attention:
+ *      cu_seqlens : device int32 [batch + 1], cu[0] = 0, non-decreasing;
+ *                   sequence b owns token rows cu[b] .. cu[b+1]-1 of q, k, v, o
+ *      q, k, v, o : [cu[batch], n_heads, d_head]
+ *      seqlen_q == seqlen_k == the longest sequence length (max_seqlen)
+ *      lse        : [batch, n_heads, max_seqlen]; row i of sequence b is
+ *                   written only for i < its length, other rows untouched.
+ *    The contents of cu_seqlens live on the device and are a precondition
+ *    (not checked): they must describe sequences of length <= max_seqlen
+ *    inside the q/k/v/o allocations.
+ *  - scale is the factor on the raw dot products (1/sqrt(d_head) is usual);
+ *    it must be finite and > 0.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *    and the call returns without synchronising.
+ *  - Argument checks are synchronous, host-only and run before any HIP call;
+ *    a call that returns an error has had no effect.  fa_last_error()
+ *    returns a message for the calling thread's last non-OK status.
+ */
+#ifndef FA_FWD_H
+#define FA_FWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_BF16 = 0, FA_FP16 = 1 } fa_dtype_t;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad scale or dtype */
+  FA_ERR_UNSUPPORTED = 2, /* d_head not in {32, 64, 128}, sizes past the 32-bit offset limit,
+                             or a tile configuration with no compiled kernel */
+  FA_ERR_MISALIGNED = 3,  /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
+  FA_ERR_HIP = 4          /* the HIP runtime reported an error (launch, timing, attributes) */
+} fa_status_t;
+
+/* A kernel tile configuration (page "Flash Attention 2 Chapter6", the
+ * Kernel 7 configuration space: block rows B_r, block columns B_c, warps;
+ * the buffering depth of the K/V stream).
+ *   br     : query rows per workgroup (B_r)
+ *   bc     : keys per K/V tile (B_c)
+ *   waves  : 64-lane wavefronts per workgroup; each owns br / waves query rows
+ *   stages : K/V tiles resident in LDS (1 = single buffer, 2 = double buffer) */
+typedef struct {
+  int br;
+  int bc;
+  int waves;
+  int stages;
+} fa_tile_config_t;
+
+/* The forward pass.  See the conventions above.  dtype is an fa_dtype_t.
+ * Returns an fa_status_t. */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
+           int seqlen_q, int seqlen_k, int n_heads, int d_head, float scale,
+           const int32_t *cu_seqlens, int dtype, void *stream);
+
+/* Tile autotuner (page "Flash Attention 2 Chapter6", Kernel 7: enumerate the
+ * configuration space, drop configurations that spill registers or do not
+ * fit, time the rest, keep the best).  Runs every compiled configuration for
+ * (dtype, d_head) that fits the LDS budget and does not spill, `reps` timed
+ * launches each after one warm-up, on the caller's buffers and stream (O and
+ * LSE are overwritten; the last launch uses the chosen configuration, so
+ * they hold its result).  Synchronises `stream`.  The winner is remembered
+ * for this (dtype, d_head, varlen, seqlen_q bucket) and used by later fa_fwd
+ * calls of that shape class (unless fa_fwd_set_config overrides it).
+ * chosen (may be NULL) receives the winner, best_ms (may be NULL) its
+ * average time per launch in milliseconds.  Arguments are checked as in
+ * fa_fwd; reps must be >= 1. */
+int fa_fwd_autotune(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
+                    int seqlen_q, int seqlen_k, int n_heads, int d_head, float scale,
+                    const int32_t *cu_seqlens, int dtype, void *stream, int reps,
+                    fa_tile_config_t *chosen, float *best_ms);
+
+/* Force the configuration fa_fwd uses for (d_head, dtype); cfg == NULL
+ * returns to automatic choice (tuned entry, else the built-in default).
+ * FA_ERR_UNSUPPORTED if no kernel was compiled for cfg. */
+int fa_fwd_set_config(int d_head, int dtype, const fa_tile_config_t *cfg);
+
+/* The configuration fa_fwd would use for this shape (host-only lookup).
+ * varlen is 0 or 1. */
+int fa_fwd_get_config(int batch, int seqlen_q, int seqlen_k, int n_heads, int d_head, int dtype,
+                      int varlen, fa_tile_config_t *out);
+
+/* Number of compiled configurations for (d_head, dtype); < 0 on bad args. */
+int fa_fwd_num_configs(int d_head, int dtype);
+
+/* Copies up to `capacity` compiled configurations for (d_head, dtype) into
+ * out; returns how many there are in total (< 0 on bad args).  Host-only. */
+int fa_fwd_list_configs(int d_head, int dtype, fa_tile_config_t *out, int capacity);
+
+/* LDS bytes a configuration uses per workgroup (stages x (K tile + V tile)),
+ * from the configuration alone.  Host-only; < 0 on bad args. */
+int fa_fwd_config_lds_bytes(int d_head, const fa_tile_config_t *cfg);
+
+/* Register and spill figures the compiler reports for a compiled
+ * configuration (hipFuncGetAttributes): vector registers per lane
+ * (architectural + accumulation), private (spill) bytes per lane, static LDS
+ * bytes.  Any output pointer may be NULL.  Needs the HIP runtime (a GPU). */
+int fa_fwd_config_resources(int d_head, int dtype, const fa_tile_config_t *cfg, int *vgprs,
+                            int *spill_bytes, int *lds_bytes);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char *fa_last_error(void);
+
+/* Library version string. */
+const char *fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_FWD_H */

@@ -1,0 +1,267 @@
+"""GPU parity: the HIP forward pass (through the C ABI) against the fp64 oracle on the
+same seeded inputs.
+
+Bar: O max-abs error <= 2e-2 and mean-abs error <= 2e-3, LSE max-abs error <= 1e-3.
+Small workloads are compared element by element in full; the full-size workloads are
+compared on sampled rows the oracle computes one by one, in the launch configuration
+the benchmark times.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_17_amd import fa, inputs
+
+pytestmark = pytest.mark.gpu
+
+O_MAX, O_MEAN, LSE_MAX = 2e-2, 2e-3, 1e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_gpu(q, k, v, scale, cu=None, max_seqlen=None, lse_fill=None):
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    cud = cu.to(dev) if cu is not None else None
+    lse = None
+    if lse_fill is not None:
+        batch = cu.numel() - 1 if cu is not None else q.shape[0]
+        nq = max_seqlen if cu is not None else q.shape[1]
+        lse = torch.full((batch, q.shape[-2], nq), lse_fill, dtype=torch.float32, device=dev)
+    o, lse = fa.fa_fwd(qd, kd, vd, lse=lse, scale=scale, cu_seqlens=cud, max_seqlen=max_seqlen)
+    torch.cuda.synchronize()
+    return o.cpu().to(torch.float64).numpy(), lse.cpu().to(torch.float64).numpy()
+
+
+def assert_close(o_gpu, o_ref, lse_gpu, lse_ref, what):
+    err = np.abs(o_gpu - o_ref)
+    lerr = np.abs(lse_gpu - lse_ref)
+    say("%s: O max %.3g mean %.3g  LSE max %.3g" % (what, err.max(), err.mean(), lerr.max()))
+    assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(lse_gpu))
+    assert err.max() <= O_MAX, what
+    assert err.mean() <= O_MEAN, what
+    assert lerr.max() <= LSE_MAX, what
+
+
+def check_dense_full(q, k, v, scale, what):
+    say("case " + what + " shape q%s k%s" % (tuple(q.shape), tuple(k.shape)))
+    o_g, lse_g = run_gpu(q, k, v, scale)
+    o_r, lse_r = oracle.attention(inputs.to_f64(q), inputs.to_f64(k), inputs.to_f64(v), scale)
+    assert_close(o_g, o_r, lse_g, lse_r, what)
+    return o_g, lse_g
+
+
+@pytest.mark.parametrize("name", ["tiny", "slice", "small_head"])
+def test_workload_full_compare(name):
+    w = inputs.workload(name)
+    check_dense_full(w["q"], w["k"], w["v"], w["scale"], name)
+
+
+def sample_rows(rng, batch, heads, lengths, n):
+    rows = []
+    for _ in range(n):
+        b = int(rng.integers(batch))
+        rows.append((b, int(rng.integers(heads)), int(rng.integers(lengths[b]))))
+    # always include the first and last rows of the first and last sequences
+    rows += [(0, 0, 0), (batch - 1, heads - 1, lengths[batch - 1] - 1)]
+    return rows
+
+
+def compare_rows(o_g, lse_g, q, k, v, scale, rows, what, cu=None, max_seqlen=None):
+    """Oracle on sampled (b, h, i) rows, one sequence at a time to keep the fp64 copies small."""
+    by_b = {}
+    for r in rows:
+        by_b.setdefault(r[0], []).append(r)
+    errs, lerrs = [], []
+    for b, rs in by_b.items():
+        if cu is None:
+            qb, kb, vb = q[b:b + 1], k[b:b + 1], v[b:b + 1]
+        else:
+            s0, s1 = int(cu[b]), int(cu[b + 1])
+            qb, kb, vb = q[None, s0:s1], k[None, s0:s1], v[None, s0:s1]
+        o_r, lse_r = oracle.attention_rows(inputs.to_f64(qb), inputs.to_f64(kb), inputs.to_f64(vb), scale,
+                                           [(0, h, i) for (_, h, i) in rs])
+        for n, (_, h, i) in enumerate(rs):
+            og = o_g[b, i, h] if cu is None else o_g[int(cu[b]) + i, h]
+            errs.append(np.abs(og - o_r[n]))
+            lerrs.append(abs(lse_g[b, h, i] - lse_r[n]))
+    err = np.concatenate(errs)
+    say("%s (%d sampled rows): O max %.3g mean %.3g  LSE max %.3g" % (what, len(rows), err.max(), err.mean(),
+                                                                      max(lerrs)))
+    assert err.max() <= O_MAX and err.mean() <= O_MEAN and max(lerrs) <= LSE_MAX, what
+
+
+def test_full_workload_sampled_rows():
+    w = inputs.workload("full")
+    say("case full B16 N4096 H16 d128 bf16")
+    o_g, lse_g = run_gpu(w["q"], w["k"], w["v"], w["scale"])
+    assert np.all(np.isfinite(o_g)) and np.all(np.isfinite(lse_g))
+    rows = sample_rows(np.random.default_rng(3), 16, 16, [4096] * 16, 160)
+    compare_rows(o_g, lse_g, w["q"], w["k"], w["v"], w["scale"], rows, "full")
+
+
+def test_varlen_workload_sampled_rows_and_padding_untouched():
+    w = inputs.workload("varlen")
+    say("case varlen lengths %s" % w["lengths"])
+    o_g, lse_g = run_gpu(w["q"], w["k"], w["v"], w["scale"], cu=w["cu_seqlens"], max_seqlen=w["max_seqlen"],
+                         lse_fill=float("nan"))
+    lens = w["lengths"]
+    for b, L in enumerate(lens):
+        assert np.all(np.isfinite(lse_g[b, :, :L]))
+        assert np.all(np.isnan(lse_g[b, :, L:])), "LSE padding rows were written"
+    assert np.all(np.isfinite(o_g))
+    rows = sample_rows(np.random.default_rng(5), len(lens), 16, lens, 160)
+    compare_rows(o_g, lse_g, w["q"], w["k"], w["v"], w["scale"], rows, "varlen", cu=w["cu_seqlens"],
+                 max_seqlen=w["max_seqlen"])
+
+
+@pytest.mark.parametrize("nq,nk,d,dtype", [
+    (128, 1, 64, "bf16"), (128, 63, 64, "bf16"), (1, 4095, 128, "bf16"), (100, 129, 128, "bf16"),
+    (129, 200, 32, "fp16"), (300, 65, 128, "fp16"), (64, 64, 32, "bf16"), (257, 1000, 64, "fp16"),
+    (33, 31, 128, "bf16"), (2, 3, 32, "bf16"),
+])
+def test_ragged_lengths(nq, nk, d, dtype):
+    q, k, v = inputs.dense_qkv(2, nq, nk, 3, d, dtype, seed=nq * 7 + nk)
+    check_dense_full(q, k, v, d ** -0.5, "ragged nq%d nk%d d%d %s" % (nq, nk, d, dtype))
+
+
+def _pad_d(x, d):
+    x = np.asarray(x, dtype=np.float32)
+    out = np.zeros((x.shape[0], d), dtype=np.float32)
+    out[:, :x.shape[1]] = x
+    return torch.from_numpy(out).to(torch.bfloat16).reshape(1, x.shape[0], 1, d)
+
+
+@pytest.mark.parametrize("case", ["hand_2x2", "hand_4x4"])
+def test_hand_cases_zero_padded(case):
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")))[case]
+    q, k, v = _pad_d(g["q"], 32), _pad_d(g["k"], 32), _pad_d(g["v"], 32)
+    o_g, lse_g = run_gpu(q, k, v, g["scale"])
+    n = len(g["q"])
+    np.testing.assert_allclose(o_g[0, :, 0, :n], np.array(g["O"]), rtol=0, atol=2e-2 * max(1, np.abs(g["O"]).max()) / 4)
+    assert np.all(o_g[0, :, 0, n:] == 0)
+    np.testing.assert_allclose(lse_g[0, 0], g["LSE"], rtol=0, atol=1e-3)
+
+
+def test_values_one_gives_ones():
+    q, k, _ = inputs.dense_qkv(2, 200, 333, 4, 128, "bf16", seed=77)
+    v = torch.ones_like(k)
+    o_g, _ = run_gpu(q, k, v, 128 ** -0.5)
+    assert np.abs(o_g - 1.0).max() <= 2 ** -8
+
+
+def test_identical_keys_give_mean_value():
+    q, k, v = inputs.dense_qkv(1, 70, 300, 2, 64, "bf16", seed=78)
+    k = k[:, :1].expand(-1, 300, -1, -1).contiguous()
+    o_g, lse_g = run_gpu(q, k, v, 0.125)
+    mean_v = inputs.to_f64(v).mean(axis=1)  # [1, H, D]
+    assert np.abs(o_g - mean_v[:, None]).max() <= O_MAX
+    s = 0.125 * np.einsum("bihd,bhd->bhi", inputs.to_f64(q), inputs.to_f64(k)[:, 0])
+    assert np.abs(lse_g - (s + np.log(300))).max() <= LSE_MAX
+
+
+def test_large_logits_stay_finite():
+    # Q, K ~ N(0, 4^2): raw scores of several hundred.
+    q, k, v = inputs.dense_qkv(1, 256, 512, 2, 128, "bf16", seed=79, std=4.0)
+    check_dense_full(q, k, v, 128 ** -0.5, "large logits")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("bf16", 32), ("fp16", 128), ("fp16", 64),
+                                     ("fp16", 32)])
+def test_every_compiled_config_matches_oracle(dtype, d):
+    q, k, v = inputs.dense_qkv(2, 333, 517, 2, d, dtype, seed=d + (1 if dtype == "fp16" else 0))
+    o_r, lse_r = oracle.attention(inputs.to_f64(q), inputs.to_f64(k), inputs.to_f64(v), d ** -0.5)
+    code = fa.FA_FP16 if dtype == "fp16" else fa.FA_BF16
+    try:
+        for c in fa.fa_fwd_list_configs(d, code):
+            fa.fa_fwd_set_config(d, code, c)
+            o_g, lse_g = run_gpu(q, k, v, d ** -0.5)
+            assert_close(o_g, o_r, lse_g, lse_r, "%s d%d %r" % (dtype, d, c))
+    finally:
+        fa.fa_fwd_set_config(d, code, None)
+
+
+def test_repeat_launches_bitwise_identical():
+    q, k, v = inputs.dense_qkv(2, 1000, 1000, 4, 128, "bf16", seed=80)
+    o1, l1 = run_gpu(q, k, v, 0.1)
+    for _ in range(3):
+        o2, l2 = run_gpu(q, k, v, 0.1)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_stages_do_not_change_bits():
+    # Same arithmetic order with single and double buffering: any difference is a race.
+    q, k, v = inputs.dense_qkv(2, 513, 700, 3, 128, "bf16", seed=81)
+    try:
+        fa.fa_fwd_set_config(128, fa.FA_BF16, (128, 64, 4, 2))
+        o2, l2 = run_gpu(q, k, v, 0.1)
+        fa.fa_fwd_set_config(128, fa.FA_BF16, (128, 64, 4, 1))
+        o1, l1 = run_gpu(q, k, v, 0.1)
+    finally:
+        fa.fa_fwd_set_config(128, fa.FA_BF16, None)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_wave_count_does_not_change_bits():
+    # Each wavefront's per-row arithmetic is the same whatever the wavefronts per workgroup.
+    q, k, v = inputs.dense_qkv(1, 600, 900, 2, 128, "bf16", seed=82)
+    outs = []
+    try:
+        for c in [(128, 64, 4, 2), (64, 64, 2, 2), (256, 64, 8, 2)]:
+            fa.fa_fwd_set_config(128, fa.FA_BF16, c)
+            outs.append(run_gpu(q, k, v, 0.1))
+    finally:
+        fa.fa_fwd_set_config(128, fa.FA_BF16, None)
+    for o, l_ in outs[1:]:
+        assert np.array_equal(o, outs[0][0]) and np.array_equal(l_, outs[0][1])
+
+
+def test_varlen_small_and_empty_sequences():
+    lens = [1, 0, 130, 64, 7, 257]
+    q, k, v, cu, mx = inputs.varlen_qkv(lengths=lens, heads=2, d_head=64, dtype="bf16", seed=83)
+    say("case varlen small lengths %s" % lens)
+    o_g, lse_g = run_gpu(q, k, v, 0.125, cu=cu, max_seqlen=mx, lse_fill=float("nan"))
+    o_r, lse_r = oracle.attention(inputs.to_f64(q), inputs.to_f64(k), inputs.to_f64(v), 0.125,
+                                  cu_seqlens=cu.numpy(), max_seqlen=mx)
+    valid = ~np.isnan(lse_r)
+    assert np.array_equal(valid, ~np.isnan(lse_g)), "LSE rows written outside sequences"
+    assert_close(o_g, o_r, lse_g[valid], lse_r[valid], "varlen small")
+
+
+def test_autotune_picks_a_compiled_config_and_leaves_valid_output():
+    q, k, v = inputs.dense_qkv(2, 512, 512, 4, 128, "bf16", seed=84)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty((2, 4, 512), dtype=torch.float32, device=dev)
+    chosen, ms = fa.fa_fwd_autotune(qd, kd, vd, o, lse, reps=2)
+    say("autotune chose %r at %.4f ms" % (chosen, ms))
+    assert chosen.as_tuple() in [c.as_tuple() for c in fa.fa_fwd_list_configs(128, fa.FA_BF16)]
+    assert ms > 0
+    o_r, lse_r = oracle.attention(inputs.to_f64(q), inputs.to_f64(k), inputs.to_f64(v), 128 ** -0.5)
+    assert_close(o.cpu().double().numpy(), o_r, lse.cpu().double().numpy(), lse_r, "autotuned")
+    got = fa.fa_fwd_get_config(2, 512, 512, 4, 128, fa.FA_BF16)
+    assert got.as_tuple() == chosen.as_tuple()
+
+
+def test_resources_reported_no_spills_in_default():
+    vgpr, spill, lds = fa.fa_fwd_config_resources(128, fa.FA_BF16, (128, 64, 4, 2))
+    say("default d128 bf16: vgprs %d spill %d lds %d" % (vgpr, spill, lds))
+    assert spill == 0 and lds == 65536
