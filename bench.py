@@ -1,0 +1,216 @@
+"""Benchmark of the attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one fa_fwd call over the whole batch of the full workload
+(B16 N4096 H16 d128 bf16, non-causal, seeded N(0,1) inputs resident in HBM before
+timing).  Prints ONE JSON line with the throughput in TFLOP/s
+(4 * B * H * Nq * Nk * d per step), the roofline figures of the kernel and the
+fp64 oracle timed on a bounded sample on the host cores.
+
+Other modes (used to produce the committed profiles):
+    --workload NAME     time another named workload (tiny, slice, full, small_head, varlen)
+    --copy-bytes N      run only a plain device copy of N bytes (the counter calibration)
+    --no-cpu-baseline   skip the oracle timing
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA: 256 CU x 4 SIMD x 1024 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    """Hash of the kernel sources; counter-derived traffic is only reported for the same kernel."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "exact_attention_17_amd", "csrc", "*"))):
+        if p.endswith((".h", ".hip", ".cpp")):
+            with open(p, "rb") as f:
+                h.update(os.path.basename(p).encode())
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/fa_fwd_<workload>_traffic.txt, "key: value" lines), if it was taken on the
+    current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "fa_fwd_%s_traffic.txt" % workload)
+    vals = {}
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.startswith("#") or ":" not in line:
+                    continue
+                key, val = line.split(":", 1)
+                vals[key.strip()] = val.strip()
+    except OSError:
+        return None
+    if vals.get("kernel_source_hash") != kernel_source_hash() or vals.get("workload") != workload:
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(nbytes, reps):
+    import torch
+    n = nbytes // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log("copy calibration: %d launches of a %d-byte device copy" % (reps, n * 4))
+
+
+def cpu_baseline(w, target_s=12.0):
+    """The oracle, as it stands, on sampled query rows of batch entry 0 (each row against all
+    keys): calibrate on a few rows, then run about target_s seconds."""
+    import numpy as np
+
+    import oracle
+    from exact_attention_17_amd import inputs
+    q = inputs.to_f64(w["q"][0:1])
+    k = inputs.to_f64(w["k"][0:1])
+    v = inputs.to_f64(w["v"][0:1])
+    nq, nk, heads, d = w["seqlen_q"], w["seqlen_k"], w["heads"], w["d_head"]
+    rng = np.random.default_rng(0)
+
+    def rows(n):
+        return [(0, int(rng.integers(heads)), int(rng.integers(nq))) for _ in range(n)]
+
+    oracle.attention_rows(q, k, v, w["scale"], rows(8))  # warm (threads, pages)
+    n = 64
+    t0 = time.perf_counter()
+    oracle.attention_rows(q, k, v, w["scale"], rows(n))
+    t = time.perf_counter() - t0
+    n = int(min(max(n * target_s / max(t, 1e-6), 64), 200000))
+    t0 = time.perf_counter()
+    oracle.attention_rows(q, k, v, w["scale"], rows(n))
+    t = time.perf_counter() - t0
+    flops = 4.0 * n * nk * d
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d random query rows of batch entry 0 (all %d keys, d %d), fp64, %.1f s" % (n, nk, d, t)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="full")
+    ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every (batch, head, query tile) is independent; see the sharding notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from exact_attention_17_amd import fa, inputs, metrics
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fa.lib()
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes, max(args.steps, 1))
+        return
+
+    dev = torch.device("cuda:0")
+    log("generating inputs for workload %s" % args.workload)
+    w = inputs.workload(args.workload)
+    qd, kd, vd = w["q"].to(dev), w["k"].to(dev), w["v"].to(dev)
+    cu = w["cu_seqlens"].to(dev) if w["cu_seqlens"] is not None else None
+    o = torch.empty_like(qd)
+    lse = torch.empty((w["batch"], w["heads"], w["seqlen_q"]), dtype=torch.float32, device=dev)
+    if cu is None:
+        flops = metrics.fwd_flops(w["batch"], w["heads"], w["seqlen_q"], w["seqlen_k"], w["d_head"])
+        nbytes = metrics.fwd_bytes(w["batch"], w["heads"], w["seqlen_q"], w["seqlen_k"], w["d_head"])
+    else:
+        flops = metrics.varlen_fwd_flops(w["lengths"], w["heads"], w["d_head"])
+        nbytes = metrics.varlen_fwd_bytes(w["lengths"], w["heads"], w["d_head"])
+    dtype_code = fa.FA_FP16 if w["dtype"] == "fp16" else fa.FA_BF16
+    cfg = fa.fa_fwd_get_config(w["batch"], w["seqlen_q"], w["seqlen_k"], w["heads"], w["d_head"], dtype_code,
+                               varlen=cu is not None)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.fa_fwd(qd, kd, vd, o, lse, scale=w["scale"], cu_seqlens=cu, max_seqlen=w["max_seqlen"],
+                  stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # Timed region: events on the stream the kernel is launched on.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    log("%s: %.4f ms per launch (wall %.4f ms), %.1f TFLOP/s, %.1f%% of %.1f, tiles %r"
+        % (args.workload, ms, wall * 1e3 / args.steps, tflops, 100 * tflops / PEAK_BF16_TFLOPS,
+           PEAK_BF16_TFLOPS, cfg))
+
+    traffic = read_traffic(args.workload)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a bounded sample")
+        cpu = cpu_baseline(w)
+        log("oracle: %.3g TFLOP/s on %d threads (%s)" % (cpu["value"], cpu["cores"], cpu["sample"]))
+
+    wl = {"full": "full B16 N4096 H16 d128 bf16 non-causal", "tiny": "tiny B1 N128 H2 d64 bf16",
+          "slice": "slice B1 Nq64 Nk4096 H1 d128 bf16", "small_head": "small_head B64 N512 H16 d32 fp16",
+          "varlen": "varlen 8 seqs U[512,8192] H16 d128 bf16"}[args.workload]
+    out = {
+        "metric": "fwd TFLOP/s (4BHN^2d) at B16 N4096 H16 d128 bf16; % of MFMA bf16 peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["dtype"],
+        "data": "synthetic (seeded N(0,1), rounded to %s)" % w["dtype"],
+        "config": {"workload": wl, "batch": w["batch"], "seq_len_q": w["seqlen_q"], "seq_len_k": w["seqlen_k"],
+                   "heads": w["heads"], "d_head": w["d_head"], "causal": False,
+                   "tile": {"br": cfg.br, "bc": cfg.bc, "waves": cfg.waves, "stages": cfg.stages},
+                   "parallelism": "single GPU"},
+        "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "algorithmic_bytes": nbytes,
+                     "algorithmic_flops": flops},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
