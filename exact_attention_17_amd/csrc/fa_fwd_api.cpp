@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -59,12 +60,12 @@ const std::vector<KernelEntry> &entries() {
 const KernelEntry *find_entry(int dtype, int d, const fa_tile_config_t &c) {
   for (const auto &e : entries())
     if (e.dtype == dtype && e.d_head == d && e.br == c.br && e.bc == c.bc && e.waves == c.waves &&
-        e.stages == c.stages)
+        e.stages == c.stages && e.schedule == c.schedule)
       return &e;
   return nullptr;
 }
 
-fa_tile_config_t cfg_of(const KernelEntry &e) { return fa_tile_config_t{e.br, e.bc, e.waves, e.stages}; }
+fa_tile_config_t cfg_of(const KernelEntry &e) { return fa_tile_config_t{e.br, e.bc, e.waves, e.stages, e.schedule}; }
 
 bool valid_dtype(int dtype) { return dtype == FA_BF16 || dtype == FA_FP16; }
 bool valid_d(int d) { return d == 32 || d == 64 || d == 128; }
@@ -81,17 +82,36 @@ int log2_bucket(int n) {
   return b;
 }
 
+// Built-in choice, from sweeps of the compiled configurations on MI355X: a short query
+// tile gains nothing from more wavefronts; at d_head 128 and longer sequences eight
+// wavefronts sharing one K/V stream per CU are fastest; otherwise two workgroups of four.
 fa_tile_config_t default_config(int seqlen_q, int d) {
-  (void)d;
-  // A single short query tile gains nothing from 4 wavefronts.
-  if (seqlen_q <= 64) return fa_tile_config_t{64, 64, 2, 2};
-  return fa_tile_config_t{128, 64, 4, 2};
+  if (seqlen_q <= 64) return fa_tile_config_t{64, 64, 2, 2, 0};
+  if (d == 128 && seqlen_q > 128) return fa_tile_config_t{256, 64, 8, 2, 0};
+  return fa_tile_config_t{128, 64, 4, 2, 0};
+}
+
+// FA_FWD_CONFIG="br,bc,waves,stages,schedule" in the environment forces that configuration
+// for every (d_head, dtype) that has it compiled (read once, at the first configuration
+// lookup; fa_fwd_set_config still overrides it).
+const fa_tile_config_t *env_config() {
+  static fa_tile_config_t cfg;
+  static bool have = false;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    const char *e = std::getenv("FA_FWD_CONFIG");
+    if (e && std::sscanf(e, "%d,%d,%d,%d,%d", &cfg.br, &cfg.bc, &cfg.waves, &cfg.stages, &cfg.schedule) == 5)
+      have = true;
+  });
+  return have ? &cfg : nullptr;
 }
 
 fa_tile_config_t choose_config(int seqlen_q, int d, int dtype, bool varlen) {
+  const fa_tile_config_t *env = env_config();
   std::lock_guard<std::mutex> lk(g_cfg_mu);
   auto f = g_forced.find({d, dtype});
   if (f != g_forced.end()) return f->second;
+  if (env && find_entry(dtype, d, *env)) return *env;
   auto t = g_tuned.find({d, dtype, varlen ? 1 : 0, log2_bucket(seqlen_q)});
   if (t != g_tuned.end()) return t->second;
   return default_config(seqlen_q, d);
@@ -157,7 +177,12 @@ int launch_entry(const KernelEntry &e, const void *q, const void *k, const void 
 
 constexpr int kLdsLimit = 160 * 1024;
 
-int lds_bytes_of(int d, const fa_tile_config_t &c) { return c.stages * 2 * c.bc * d * 2; }
+// K and V tiles resident in LDS: stages (K, V) pairs for schedules 0 and 2; a 2-slot K ring
+// plus a 3-slot V ring for schedule 1.
+int lds_bytes_of(int d, const fa_tile_config_t &c) {
+  const int tile = c.bc * d * 2;
+  return c.schedule == 1 ? 5 * tile : c.stages * 2 * tile;
+}
 
 }  // namespace
 

@@ -14,12 +14,12 @@
 //
 // gfx950 mapping (a design of its own; the pages' Ampere fragments,
 // ldmatrix and cp.async do not exist here):
-//  * Each wavefront owns 32 query rows.  Scores are formed transposed,
-//    S^T = K Q^T, with v_mfma_f32_32x32x16 (A = 32 keys x 16 d read from
-//    LDS, B = 16 d x 32 queries held in registers for the whole loop).  In
-//    the 32x32 accumulator lane l holds query l%32 and 16 of the 32 keys
-//    (rows 8g + 4(l/32) + r%4), so a row's max and sum need one exchange
-//    between lanes l and l+32 (v_permlane32_swap).
+//  * A block of 32 query rows is the unit of work.  Scores are formed
+//    transposed, S^T = K Q^T, with v_mfma_f32_32x32x16 (A = 32 keys x 16 d
+//    read from LDS, B = 16 d x 32 queries held in registers for the whole
+//    loop).  In the 32x32 accumulator lane l holds query l%32 and 16 of the
+//    32 keys (rows 8g + 4(l/32) + r%4), so a row's max and sum need one
+//    exchange between lanes l and l+32 (v_permlane32_swap).
 //  * The same registers, rounded to 16 bits, are directly the B operand of
 //    O^T = V^T P^T (v_mfma_f32_32x32x16 again).  The key order inside each
 //    16-key step is the accumulator's row order; the A operand (V^T, 32 d x
@@ -27,17 +27,42 @@
 //    ds_read_b64_tr_b16, which returns four keys of one d column per lane.
 //  * K and V tiles go from HBM to LDS with buffer_load_dwordx4 ... lds
 //    (no registers, no LDS write instructions); rows past the end of the
-//    sequence are out of the buffer's range and read as zero.  Tiles are
-//    double buffered: tile j+1 is in flight while tile j is used.
+//    sequence are out of the buffer's range and read as zero.  The next
+//    tiles are in flight while the current ones are used.
 //  * LDS rows are XOR-swizzled in 16-byte chunks so that both the K reads
 //    (16 B per lane, 32 rows) and the transposed V reads (8 B per lane,
 //    8 rows x 4 chunks) spread over all banks.
 //  * Workgroups are renumbered so that the query tiles of one (batch, head)
 //    run on the same XCD and share its L2 for K/V.
+//
+// Three schedules:
+//  SCHED 0: each wavefront owns one 32-row block and runs QK^T, softmax and
+//    PV of a tile in turn (two wavefronts per SIMD hide each other's stalls).
+//  SCHED 1: each wavefront owns two 32-row blocks A and B (one wavefront per
+//    SIMD, 512 registers) and software-pipelines them so that the softmax of
+//    one block (vector ALU) is issued between the matrix instructions of the
+//    other: per step j,
+//      1. QK_A(j)            alongside  softmax_B(j-1)
+//      2. PV_B(j-1)          alongside  softmax_A(j)
+//      3. QK_B(j)
+//      4. PV_A(j)
+//    (the overlap of softmax with matrix work is the point of the ping-pong
+//    and intra-warpgroup pipelining of page "GPU 内核与 FlashAttention",
+//    sections 15.3-15.4, done here inside one wavefront).  K tiles use a
+//    2-slot ring and V tiles a 3-slot ring, since step j reads K(j), V(j) and
+//    V(j-1) while K(j+1) and V(j+1) are in flight.
+//  SCHED 2: eight wavefronts, each owning one 32-row block, in two groups of
+//    four (one wavefront of each group per SIMD).  A workgroup barrier splits
+//    every step into a matrix half (PV of the previous tile, QK^T of this
+//    one) and a softmax half, and the second group runs one half behind the
+//    first: the ping-pong of page "GPU 内核与 FlashAttention", section 15.3,
+//    with one barrier in place of named barriers.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "fa_internal.h"
 
@@ -58,6 +83,9 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // s_waitcnt immediate for "vmcnt(0)" with the other counters left alone (gfx9 encoding:
 // vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
 constexpr int kWaitVmcnt0 = 0x0F70;
+// The running max used as the exponent reference moves only when a tile's row max exceeds
+// it by more than this many powers of two (so unnormalised terms stay below 2^8).
+constexpr float kLazyRescale = 8.0f;
 // Dword 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle).
 constexpr int kBufferFlags = 0x00020000;
 
@@ -115,23 +143,280 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                            kBufferFlags);
 }
 
-template <int D, int BR, int BC, int NW, int STAGES, bool F16>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+// s_waitcnt vmcnt(N) with the other counters left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Calls f(integral_constant<int, I>) for I = B .. E-1 (indices usable as immediates).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Per-lane LDS read offsets.  With the XOR swizzle they are not affine in the unrolled loop
+// indices, but each splits into a per-lane base plus (constant XOR per-lane mask):
+//   K operand (t = 16-wide d step, kb = 32-key block):
+//     kr*ROWB + (((2t + hi) ^ g) << 4) = kbase + ((32 t) ^ kx) + kb*32*ROWB, g = swz(kr)
+//   V^T operand (dt = 32-wide d tile, ks = 16-key step, rho = which four keys):
+//     r*ROWB + ((chunk ^ swz(r)) << 4) + 8 half = vbase[rho] + ((64 dt) ^ vx[rho]) + 16 ks*ROWB
+// (swz(r) does not depend on ks: the keys of step ks are rows 16 ks + ..., and swz only looks
+// at the low four row bits in a way a multiple of 16 leaves alone).
+struct LdsAddr {
+  int kbase, kx, vbase0, vbase1, vx0, vx1;
+};
+
+template <int D>
+__device__ __forceinline__ LdsAddr lds_addr(int lane) {
+  constexpr int ROWB = D * 2;
+  const int kr = lane & 31, hi = (lane >> 5) & 1, l16 = lane & 15, g2 = (lane >> 4) & 1;
+  const int gk = swz<D>(kr);
+  LdsAddr ad;
+  ad.kbase = kr * ROWB + ((hi ^ (gk & 1)) << 4);
+  ad.kx = (gk >> 1) << 5;
+  const int a = l16 >> 2;                       // row within the four keys of a read
+  const int x = 2 * g2 + ((l16 & 3) >> 1);      // chunk within the 32-wide d tile
+  const int half = l16 & 1;
+  const int r0 = 4 * hi + a, r1 = 8 + 4 * hi + a;
+  const int gv0 = swz<D>(r0), gv1 = swz<D>(r1);
+  ad.vbase0 = r0 * ROWB + ((x ^ (gv0 & 3)) << 4) + half * 8;
+  ad.vbase1 = r1 * ROWB + ((x ^ (gv1 & 3)) << 4) + half * 8;
+  ad.vx0 = (gv0 >> 2) << 6;
+  ad.vx1 = (gv1 >> 2) << 6;
+  return ad;
+}
+
+// LDS reads as inline assembly.  The compiler neither knows which LDS bytes a transposing
+// read touches (it would otherwise wait for every LDS DMA in flight, the prefetch of later
+// tiles, before each one) nor keeps enough reads in flight ahead of the MFMAs that consume
+// them; so reads are issued here a fixed distance ahead and their completion is awaited
+// explicitly.  LDS operations complete in issue order, so "at most N outstanding" means all
+// but the N most recent reads are done.  lds_dep makes a register look redefined after the
+// wait, so that its consumer cannot be scheduled above the wait.
+template <int OFF>
+__device__ __forceinline__ void lds_read_b128(i32x4 &r, uint32_t addr) {
+  __asm__ volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void lds_read_tr(i16x4 &r, uint32_t addr) {
+  __asm__ volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+}
+template <int N>
+__device__ __forceinline__ void lds_wait() {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt field");
+  __asm__ volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N));
+}
+template <typename T>
+__device__ __forceinline__ void lds_dep(T &r) {
+  __asm__ volatile("" : "+v"(r));
+}
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// S^T = K_tile Q^T for one 32-query block: KB accumulators of 32 keys x 32 queries.  MFMA i
+// (t = i / KB, kb = i % KB) reads its K operand LA reads ahead.
+template <int D, int BC, bool F16, int LA = 6>
+__device__ __forceinline__ void qk_block(const char *sk, f32x16 (&S)[BC / 32], const i32x4 (&qr)[D / 16],
+                                         const LdsAddr &ad) {
+  constexpr int ROWB = D * 2, KB = BC / 32, T = D / 16, N = T * KB;
+  constexpr int L = LA < N ? LA : N;
+  const uint32_t sk_lds = (uint32_t)(uintptr_t)(const char FA_LDS *)sk;
+  uint32_t koff[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) koff[t] = sk_lds + (uint32_t)(((32 * t) ^ ad.kx) + ad.kbase);
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) S[kb] = f32x16{};
+  i32x4 buf[L + 1];
+  auto issue = [&buf, &koff](auto i_c) __attribute__((always_inline)) {
+    constexpr int i = decltype(i_c)::value;
+    lds_read_b128<(i % KB) * 32 * ROWB>(buf[i % (L + 1)], koff[i / KB]);
+  };
+  static_for<0, L>(issue);
+  static_for<0, N>([&](auto i_c) __attribute__((always_inline)) {
+    constexpr int i = decltype(i_c)::value;
+    if constexpr (i + L < N) issue(IC<i + L>{});
+    constexpr int after = (N - 1 - i) < L ? (N - 1 - i) : L;  // reads issued after read i
+    lds_wait<after>();
+    lds_dep(buf[i % (L + 1)]);
+    S[i % KB] = mfma32<F16>(buf[i % (L + 1)], qr[i / KB], S[i % KB]);
+  });
+}
+
+// O^T += V_tile^T P~^T for one 32-query block.  Lane l's A operand: d = 32 dt + l%32, keys
+// 16 ks + 4(l/32) + {0..3} and 16 ks + 8 + 4(l/32) + {0..3}: two transposed reads, each fed
+// by lanes that point at four rows x 4 consecutive d of the row-major V tile.  MFMA i
+// (ks = i / DT, dt = i % DT) has its two reads issued LA MFMAs ahead.
+template <int D, int BC, bool F16, int LA = 4>
+__device__ __forceinline__ void pv_block(const char *sv, const i32x4 (&P)[BC / 16], f32x16 (&O)[D / 32],
+                                         const LdsAddr &ad) {
+  constexpr int ROWB = D * 2, DT = D / 32, KS = BC / 16, N = KS * DT;
+  constexpr int L = LA < N ? LA : N;
+  static_assert(2 * L <= 15, "lgkmcnt field");
+  const uint32_t sv_lds = (uint32_t)(uintptr_t)(const char FA_LDS *)sv;
+  uint32_t a0[DT], a1[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    a0[dt] = sv_lds + (uint32_t)(((64 * dt) ^ ad.vx0) + ad.vbase0);
+    a1[dt] = sv_lds + (uint32_t)(((64 * dt) ^ ad.vx1) + ad.vbase1);
+  }
+  i16x4 b0[L + 1], b1[L + 1];
+  auto issue = [&b0, &b1, &a0, &a1](auto i_c) __attribute__((always_inline)) {
+    constexpr int i = decltype(i_c)::value;
+    lds_read_tr<16 * (i / DT) * ROWB>(b0[i % (L + 1)], a0[i % DT]);
+    lds_read_tr<16 * (i / DT) * ROWB>(b1[i % (L + 1)], a1[i % DT]);
+  };
+  static_for<0, L>(issue);
+  static_for<0, N>([&](auto i_c) __attribute__((always_inline)) {
+    constexpr int i = decltype(i_c)::value;
+    if constexpr (i + L < N) issue(IC<i + L>{});
+    constexpr int after = 2 * ((N - 1 - i) < L ? (N - 1 - i) : L);  // reads issued after MFMA i's
+    lds_wait<after>();
+    lds_dep(b0[i % (L + 1)]);
+    lds_dep(b1[i % (L + 1)]);
+    const i16x4 &v0 = b0[i % (L + 1)], &v1 = b1[i % (L + 1)];
+    const i16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    O[i % DT] = mfma32<F16>(__builtin_bit_cast(i32x4, va), P[i / DT], O[i % DT]);
+  });
+}
+
+// Online softmax step of one 32-query block on the raw scores S of tile j (keys from
+// kvalid on, when MASK, are past the sequence end).  Leaves P~ (16-bit PV operands) in P,
+// updates m and l, and returns alpha, the factor O must be multiplied by before this tile's
+// PV; rescale is false when no row of the wavefront needs it (alpha is then 1 everywhere).
+// The reference max m only moves when this tile's row max exceeds it by more than
+// kLazyRescale in exp2 units; otherwise the exponentials are taken against the old m (they
+// stay below 2^kLazyRescale), and the rescale of O and l, an exact identity whichever
+// reference is used, is skipped.
+template <int BC, bool F16, bool MASK>
+__device__ __forceinline__ float softmax_block(f32x16 (&S)[BC / 32], i32x4 (&P)[BC / 16], float &m, float &l,
+                                               float c, int kvalid_lane, bool &rescale) {
+  constexpr int KB = BC / 32;
+  if constexpr (MASK) {
+    // key of accumulator register r in block kb is kb*32 + 8(r/4) + 4 hi + r%4; the lane part
+    // 4 hi is already taken off kvalid_lane so that the compared constants are immediates
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kb * 32 + 8 * (r >> 2) + (r & 3) >= kvalid_lane) S[kb][r] = -INFINITY;
+  }
+  float mx = S[0][0];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
+  mx = pair_max(mx);
+  const bool grow = (mx - m) * c > kLazyRescale;  // always true on the first tile (m = -inf)
+  const float m_new = grow ? mx : m;
+  const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);  // 0 on the first tile, else <= 1
+  rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
+  m = m_new;
+  const float mc = m * c;
+  float rs = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], c, -mc));
+      S[kb][r] = p;
+      rs += p;
+    }
+  l = l * alpha + rs;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        P[2 * kb + s2][e] = pack2<F16>(S[kb][8 * s2 + 2 * e], S[kb][8 * s2 + 2 * e + 1]);
+  return alpha;
+}
+
+template <int DT>
+__device__ __forceinline__ void rescale_o(f32x16 (&O)[DT], float alpha) {
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) O[dt] *= alpha;
+}
+
+// Finish one 32-query block: total the row sum over the lane pair, normalise, store O (16-bit)
+// and LSE.  qrow0 is the block's first row in the sequence.
+template <int D, bool F16>
+__device__ __forceinline__ void store_block(const f32x16 (&O)[D / 32], float m, float l, float c, int qrow0,
+                                            int nq, uint32_t row_bytes, const __amdgpu_buffer_rsrc_t &ro,
+                                            float *lse_row, int lane) {
+  constexpr int DT = D / 32;
+  const int hi = lane >> 5;
+  l = pair_sum(l);
+  const float inv = 1.f / l;
+  const int qrow = qrow0 + (lane & 31);
+  if (hi == 0 && qrow < nq) {
+    // LSE = scale * m + ln l = ln2 * (m * c + log2 l)
+    lse_row[qrow] = 0.69314718055994531f * __builtin_fmaf(m, c, __builtin_amdgcn_logf(l));
+  }
+  const uint32_t o_off = (uint32_t)qrow * row_bytes + hi * 16;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      // Accumulator groups g0 = 2p, g1 = 2p+1 hold d = 32dt + 8g + 4(l/32) + {0..3}.  After
+      // swapping one half-group across the lane pair, lanes < 32 own d = 32dt + 16p + 0..7
+      // and lanes >= 32 own d = 32dt + 16p + 8..15.
+      const int g0 = 2 * p, g1 = 2 * p + 1;
+      const int x0 = pack2<F16>(O[dt][4 * g0 + 0] * inv, O[dt][4 * g0 + 1] * inv);
+      const int x1 = pack2<F16>(O[dt][4 * g0 + 2] * inv, O[dt][4 * g0 + 3] * inv);
+      const int y0 = pack2<F16>(O[dt][4 * g1 + 0] * inv, O[dt][4 * g1 + 1] * inv);
+      const int y1 = pack2<F16>(O[dt][4 * g1 + 2] * inv, O[dt][4 * g1 + 3] * inv);
+      auto s0 = __builtin_amdgcn_permlane32_swap((unsigned)x0, (unsigned)y0, false, false);
+      auto s1 = __builtin_amdgcn_permlane32_swap((unsigned)x1, (unsigned)y1, false, false);
+      const i32x4 out = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+      // rows past nq are out of the buffer's range: the store is dropped
+      __builtin_amdgcn_raw_buffer_store_b128(out, ro, o_off + (32 * dt + 16 * p) * 2, 0, 0);
+    }
+  }
+}
+
+template <int SCHED>
+constexpr int waves_per_simd() {
+  return SCHED == 1 ? 1 : 2;
+}
+
+// Workgroup barrier without the memory fences of __syncthreads (which would also wait for
+// the LDS DMA of later tiles still in flight); the empty asm statements keep the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void wg_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+template <int D, int BR, int BC, int NW, int STAGES, bool F16, int SCHED>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_per_simd<SCHED>())))
 fa_fwd_kernel(FaArgs a) {
-  constexpr int QW = 32;          // query rows per wavefront
-  constexpr int ROWB = D * 2;     // bytes of one row of a tile
-  constexpr int TILE = BC * ROWB; // bytes of one K (or V) tile
-  constexpr int STAGE = 2 * TILE; // K tile then V tile
-  constexpr int NCH = TILE / 1024;  // 1 KB pieces per tile (64 lanes x 16 B)
-  constexpr int DT = D / 32;      // 32-wide d tiles of the output
-  constexpr int KB = BC / 32;     // 32-key blocks per tile
-  constexpr int KS = BC / 16;     // 16-key MFMA steps per tile
-  static_assert(BR == NW * QW, "each wavefront owns 32 query rows");
+  constexpr int NB = SCHED == 1 ? 2 : 1;  // 32-query blocks per wavefront
+  constexpr int QW = 32 * NB;             // query rows per wavefront
+  constexpr int ROWB = D * 2;             // bytes of one row of a tile
+  constexpr int TILE = BC * ROWB;         // bytes of one K (or V) tile
+  constexpr int NCH = TILE / 1024;        // 1 KB pieces per tile (64 lanes x 16 B)
+  constexpr int DT = D / 32;              // 32-wide d tiles of the output
+  constexpr int KB = BC / 32;             // 32-key blocks per tile
+  constexpr int KS = BC / 16;             // 16-key MFMA steps per tile
+  // LDS: SCHED 0 holds STAGES (K, V) tile pairs; SCHED 1 a 2-slot K ring and a 3-slot V ring.
+  constexpr int LDS_BYTES = SCHED == 1 ? 5 * TILE : STAGES * 2 * TILE;  // SCHED 2: 2 K + 2 V slots
+  static_assert(BR == NW * QW, "rows per workgroup");
   static_assert(D == 32 || D == 64 || D == 128, "d_head");
   static_assert(BC % 32 == 0 && TILE % 1024 == 0, "tile shape");
-  static_assert(STAGES == 1 || STAGES == 2, "stages");
+  static_assert(STAGES >= 1 && STAGES <= 4, "stages");
+  static_assert(SCHED == 0 || (SCHED == 1 && STAGES == 2) || (SCHED == 2 && STAGES == 2 && NW == 8),
+                "schedule");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -174,184 +459,215 @@ fa_fwd_kernel(FaArgs a) {
   const auto rk = make_rsrc(kb_, (uint32_t)(nk - 1) * row_bytes + ROWB);
   const auto rv = make_rsrc(vb, (uint32_t)(nk - 1) * row_bytes + ROWB);
   const auto ro = make_rsrc(ob, (uint32_t)(nq - 1) * row_bytes + ROWB);
+  float *lse_row = a.lse + ((int64_t)b * a.heads + h) * a.seqlen_q;
 
-  // This lane's query row; Q stays in registers as the B operand (16 d per step).
-  const int qrow = q_tile0 + wave * QW + (lane & 31);
-  i32x4 qreg[D / 16];
+  // Q stays in registers as the B operand (16 d per step) of each 32-row block.
+  const int wrow0 = q_tile0 + wave * QW;  // first row of this wavefront
+  i32x4 qreg[NB][D / 16];
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t)
-    qreg[t] = __builtin_amdgcn_raw_buffer_load_b128(rq, (uint32_t)qrow * row_bytes + (2 * t + hi) * 16, 0, 0);
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+      qreg[nb][t] = __builtin_amdgcn_raw_buffer_load_b128(
+          rq, (uint32_t)(wrow0 + 32 * nb + (lane & 31)) * row_bytes + (2 * t + hi) * 16, 0, 0);
 
-  // Issue the loads of K/V tile j into LDS stage st: piece u of a tile is 1 KB, filled by
-  // one wavefront instruction; lane i's 16 bytes land at piece + 16 i, so each lane fetches
-  // the global chunk that the swizzled layout puts there.
-  auto load_tile = [&](int j, int st) {
-    char *sk = smem + st * STAGE;
-    char *sv = sk + TILE;
+  // Issue the loads of tile j of K (or V) into LDS at dst: piece u of a tile is 1 KB, filled
+  // by one wavefront instruction; lane i's 16 bytes land at piece + 16 i, so each lane
+  // fetches the global chunk that the swizzled layout puts there.  LW wavefronts share the
+  // pieces, this one being number lw among them.
+  auto load_by = [&](const __amdgpu_buffer_rsrc_t &rsrc, char *dst, int j, int lw, auto lw_c)
+                     __attribute__((always_inline)) {
+    constexpr int LW = decltype(lw_c)::value;
     const uint32_t tile_off = (uint32_t)(j * BC) * row_bytes;
 #pragma unroll
-    for (int i = 0; i < (NCH + NW - 1) / NW; ++i) {
-      const int u = wave + i * NW;
-      if (NCH % NW == 0 || u < NCH) {
+    for (int i = 0; i < (NCH + LW - 1) / LW; ++i) {
+      const int u = lw + i * LW;
+      if (NCH % LW == 0 || u < NCH) {
         const int pos = u * 1024 + lane * 16;
         const int r = pos / ROWB;
-        const int c = ((pos % ROWB) >> 4) ^ swz<D>(r);
-        const uint32_t goff = tile_off + (uint32_t)r * row_bytes + c * 16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (void FA_LDS *)(sk + u * 1024), 16, goff, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (void FA_LDS *)(sv + u * 1024), 16, goff, 0, 0, 0);
+        const int cc = ((pos % ROWB) >> 4) ^ swz<D>(r);
+        const uint32_t goff = tile_off + (uint32_t)r * row_bytes + cc * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void FA_LDS *)(dst + u * 1024), 16, goff, 0, 0, 0);
       }
     }
   };
+  auto load_one = [&](const __amdgpu_buffer_rsrc_t &rsrc, char *dst, int j) __attribute__((always_inline)) {
+    load_by(rsrc, dst, j, wave, std::integral_constant<int, NW>{});
+  };
 
-  f32x16 O[DT];
+  f32x16 O[NB][DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) O[dt] = f32x16{};
-  float m = -INFINITY;  // running max of raw scores (both lanes of a pair hold the same)
-  float l = 0.f;        // this lane's share of the running sum of exp2 terms
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) O[nb][dt] = f32x16{};
+  float m[NB], l[NB];  // running max of raw scores (same on both lanes of a pair); lane's sum share
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    m[nb] = -INFINITY;
+    l[nb] = 0.f;
+  }
   const float c = a.scale_log2;
-
-  const int kr = lane & 31;
-  const int ksw = swz<D>(kr);
-  const int l16 = lane & 15;
-  const int g2 = (lane >> 4) & 1;
+  const LdsAddr ad = lds_addr<D>(lane);
 
   const int nkt = (nk + BC - 1) / BC;
-  load_tile(0, 0);
-  for (int j = 0; j < nkt; ++j) {
-    const int st = (STAGES == 2) ? (j & 1) : 0;
-    if constexpr (STAGES == 1) {
-      if (j > 0) {
-        __syncthreads();  // everyone is done with tile j-1
-        load_tile(j, 0);
+  const int nfull = nk / BC;  // tiles with no key past the end
+  auto softmax = [&](f32x16 (&S)[KB], i32x4 (&P)[KS], int nb, int j, bool &rescale) __attribute__((always_inline)) {
+    if (j < nfull) return softmax_block<BC, F16, false>(S, P, m[nb], l[nb], c, 0, rescale);
+    return softmax_block<BC, F16, true>(S, P, m[nb], l[nb], c, nk - j * BC - 4 * hi, rescale);
+  };
+
+  if constexpr (SCHED == 0) {
+    // STAGES (K, V) tile pairs in LDS, tile j in stage j % STAGES; tile j + STAGES - 1 is
+    // requested at the start of step j (its stage held tile j - 1, which every wavefront
+    // finished before the barrier that opens step j), so STAGES - 1 tiles are in flight.
+    constexpr int STAGE = 2 * TILE;  // K tile then V tile
+    constexpr int LPT = 2 * (NCH >= NW ? NCH / NW : 1);  // loads per tile of a loading wavefront
+    static_assert(NCH % NW == 0 || NW % NCH == 0, "tile pieces spread evenly");
+    auto step = [&](auto st_c, int j) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st_c)::value;
+      if constexpr (STAGES == 1) {
+        if (j > 0) {
+          __syncthreads();  // everyone is done with tile j-1
+          load_one(rk, smem, j);
+          load_one(rv, smem + TILE, j);
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      } else {
+        // this wavefront's pieces of tile j landed: at most the later tiles' loads pending
+        const int ahead = min(STAGES - 2, nkt - 1 - j);
+        if (ahead <= 0)
+          wait_vmcnt<0>();
+        else if (STAGES < 4 || ahead == 1)
+          wait_vmcnt<LPT>();
+        else
+          wait_vmcnt<2 * LPT>();
+      }
+      wg_barrier();  // ... and everyone's; and everyone is done with tile j - 1
+      if constexpr (STAGES >= 2) {
+        constexpr int NS = (ST + STAGES - 1) % STAGES;  // stage of tile j + STAGES - 1
+        if (j + STAGES - 1 < nkt) {
+          load_one(rk, smem + NS * STAGE, j + STAGES - 1);
+          load_one(rv, smem + NS * STAGE + TILE, j + STAGES - 1);
+        }
+      }
+      f32x16 S[KB];
+      i32x4 P[KS];
+      bool rs;
+      qk_block<D, BC, F16>(smem + ST * STAGE, S, qreg[0], ad);
+      const float alpha = softmax(S, P, 0, j, rs);
+      if (rs) rescale_o<DT>(O[0], alpha);
+      pv_block<D, BC, F16>(smem + ST * STAGE + TILE, P, O[0], ad);
+    };
+#pragma unroll
+    for (int t = 0; t < (STAGES > 1 ? STAGES - 1 : 1); ++t) {
+      if (t < nkt) {
+        load_one(rk, smem + t * STAGE, t);
+        load_one(rv, smem + t * STAGE + TILE, t);
       }
     }
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wavefront's pieces of tile j landed
-    __syncthreads();                          // ... and everyone's
-    if constexpr (STAGES == 2) {
-      if (j + 1 < nkt) load_tile(j + 1, (j + 1) & 1);
+    for (int j = 0; j < nkt; j += STAGES) {
+      static_for<0, STAGES>([&](auto st_c) __attribute__((always_inline)) {
+        if (j + decltype(st_c)::value < nkt) step(st_c, j + decltype(st_c)::value);
+      });
     }
-    const char *sk = smem + st * STAGE;
-    const char *sv = sk + TILE;
-
-    // S^T = K_j Q^T for this wavefront's 32 queries: KB accumulators of 32 keys x 32 queries.
+    store_block<D, F16>(O[0], m[0], l[0], c, wrow0, nq, row_bytes, ro, lse_row, lane);
+  } else if constexpr (SCHED == 1) {
+    // Dual-block software pipeline (see the header comment).  Step j:
+    //   issue loads K(j+1) -> K slot (j+1)%2 (held K(j-1), last read in step j-1) and
+    //                V(j+1) -> V slot (j+1)%3 (held V(j-2), last read in step j-1);
+    //   1. QK_A(j) [K slot j%2]            with softmax_B(j-1)
+    //   2. PV_B(j-1) [V slot (j-1)%3]      with softmax_A(j)
+    //   3. QK_B(j) [K slot j%2]
+    //   4. PV_A(j) [V slot j%3]
+    // Loads issued at the start of step j are waited for at the start of step j+1.
+    f32x16 S[2][KB];
+    i32x4 P[2][KS];
+    float alpha[2] = {1.f, 1.f};
+    bool rs[2] = {false, false};
+    auto kslot = [&](int j) __attribute__((always_inline)) { return smem + (j & 1) * TILE; };
+    auto vslot = [&](int j) __attribute__((always_inline)) { return smem + 2 * TILE + (j % 3) * TILE; };
+    load_one(rk, kslot(0), 0);
+    load_one(rv, vslot(0), 0);
+    for (int j = 0; j <= nkt; ++j) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      if (j + 1 < nkt) {
+        load_one(rk, kslot(j + 1), j + 1);
+        load_one(rv, vslot(j + 1), j + 1);
+      }
+      // 1.
+      if (j < nkt) qk_block<D, BC, F16>(kslot(j), S[0], qreg[0], ad);
+      if (j >= 1) alpha[1] = softmax(S[1], P[1], 1, j - 1, rs[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      // 2.
+      if (j >= 1) {
+        if (rs[1]) rescale_o<DT>(O[1], alpha[1]);
+        pv_block<D, BC, F16>(vslot(j - 1), P[1], O[1], ad);
+      }
+      if (j < nkt) alpha[0] = softmax(S[0], P[0], 0, j, rs[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      // 3. and 4.
+      if (j < nkt) {
+        qk_block<D, BC, F16>(kslot(j), S[1], qreg[1], ad);
+        if (rs[0]) rescale_o<DT>(O[0], alpha[0]);
+        pv_block<D, BC, F16>(vslot(j), P[0], O[0], ad);
+      }
+    }
+    store_block<D, F16>(O[0], m[0], l[0], c, wrow0, nq, row_bytes, ro, lse_row, lane);
+    store_block<D, F16>(O[1], m[1], l[1], c, wrow0 + 32, nq, row_bytes, ro, lse_row, lane);
+  } else {
+    // Ping-pong over two groups of four wavefronts (see the header comment).  Every
+    // wavefront runs the same program, step j = MMA(j) | barrier | SM(j) | barrier, where
+    // MMA(j) = PV(j-1) + QK(j) and SM(j) is the softmax of tile j; group 1 starts one
+    // barrier later, so on each SIMD (one wavefront of each group) one wavefront issues
+    // matrix instructions while the other runs its softmax.  K(j) and V(j-1) are read in the
+    // two halves around the middle barrier of group 0's step j.  Group 0 issues the loads of
+    // K(j+1) (into K slot (j+1)&1, whose K(j-1) was last read before the barrier that starts
+    // this step) and V(j) (into V slot j&1, holding V(j-2)) at the start of its step j and
+    // waits for them at its end, one barrier before anyone reads them.
+    const int grp = wave >> 2;
+    const int gw = wave & 3;
+    using Four = std::integral_constant<int, 4>;
     f32x16 S[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) S[kb] = f32x16{};
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const i32x4 ka = *(const i32x4 *)(sk + (kb * 32 + kr) * ROWB + (((2 * t + hi) ^ ksw) << 4));
-        S[kb] = mfma32<F16>(ka, qreg[t], S[kb]);
-      }
-    }
-
-    // Keys past the end of the sequence (last tile only) get -inf.
-    const int kvalid = nk - j * BC;
-    if (kvalid < BC) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3) >= kvalid) S[kb][r] = -INFINITY;
-    }
-
-    // Online softmax step.
-    float mx = S[0][0];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
-    mx = pair_max(mx);
-    const float m_new = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
-    const float mc = m_new * c;
-    m = m_new;
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], c, -mc));
-        S[kb][r] = p;
-        rs += p;
-      }
-    l = l * alpha + rs;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) O[dt] *= alpha;
-
-    // P~ as 16-bit B operands, one per 16-key step.
     i32x4 P[KS];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          P[2 * kb + s2][e] = pack2<F16>(S[kb][8 * s2 + 2 * e], S[kb][8 * s2 + 2 * e + 1]);
-
-    // O^T += V_j^T P~^T.  Lane l's A operand: d = 32 dt + l%32, keys 16 ks + 4(l/32) + {0..3}
-    // and 16 ks + 8 + 4(l/32) + {0..3}: two transposed reads, each fed by lanes that point at
-    // four rows x 4 consecutive d of the row-major V tile.
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int col = 32 * dt + 16 * g2 + 4 * (l16 & 3);
-        const int chunk = col >> 3;
-        const int half = l16 & 1;
-        const int r0 = 16 * ks + 4 * hi + (l16 >> 2);
-        const int r1 = r0 + 8;
-        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (i16x4 FA_LDS *)(sv + r0 * ROWB + ((chunk ^ swz<D>(r0)) << 4) + half * 8));
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (i16x4 FA_LDS *)(sv + r1 * ROWB + ((chunk ^ swz<D>(r1)) << 4) + half * 8));
-        const i16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        O[dt] = mfma32<F16>(__builtin_bit_cast(i32x4, va), P[ks], O[dt]);
+    auto kslot = [&](int j) __attribute__((always_inline)) { return smem + (j & 1) * TILE; };
+    auto vslot = [&](int j) __attribute__((always_inline)) { return smem + 2 * TILE + (j & 1) * TILE; };
+    load_one(rk, kslot(0), 0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    wg_barrier();
+    if (grp == 1) wg_barrier();
+    for (int j = 0; j <= nkt; ++j) {
+      if (grp == 0) {
+        if (j + 1 < nkt) load_by(rk, kslot(j + 1), j + 1, gw, Four{});
+        if (j < nkt) load_by(rv, vslot(j), j, gw, Four{});
       }
+      if (j >= 1) pv_block<D, BC, F16>(vslot(j - 1), P, O[0], ad);
+      if (j < nkt) qk_block<D, BC, F16>(kslot(j), S, qreg[0], ad);
+      wg_barrier();
+      if (j < nkt) {
+        bool rs;
+        const float alpha = softmax(S, P, 0, j, rs);
+        if (rs) rescale_o<DT>(O[0], alpha);
+      }
+      if (grp == 0) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      wg_barrier();
     }
-  }
-
-  // Epilogue: finish the row sum over the lane pair, normalise, store O and LSE.
-  l = pair_sum(l);
-  const float inv = 1.f / l;
-  if (hi == 0 && qrow < nq) {
-    // LSE = scale * m + ln l = ln2 * (m * c + log2 l)
-    a.lse[((int64_t)b * a.heads + h) * a.seqlen_q + qrow] =
-        0.69314718055994531f * __builtin_fmaf(m, c, __builtin_amdgcn_logf(l));
-  }
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      // Accumulator groups g0 = 2p, g1 = 2p+1 hold d = 32dt + 8g + 4(l/32) + {0..3}.  After
-      // swapping one half-group across the lane pair, lanes < 32 own d = 32dt + 16p + 0..7
-      // and lanes >= 32 own d = 32dt + 16p + 8..15.
-      const int g0 = 2 * p, g1 = 2 * p + 1;
-      const int x0 = pack2<F16>(O[dt][4 * g0 + 0] * inv, O[dt][4 * g0 + 1] * inv);
-      const int x1 = pack2<F16>(O[dt][4 * g0 + 2] * inv, O[dt][4 * g0 + 3] * inv);
-      const int y0 = pack2<F16>(O[dt][4 * g1 + 0] * inv, O[dt][4 * g1 + 1] * inv);
-      const int y1 = pack2<F16>(O[dt][4 * g1 + 2] * inv, O[dt][4 * g1 + 3] * inv);
-      auto s0 = __builtin_amdgcn_permlane32_swap((unsigned)x0, (unsigned)y0, false, false);
-      auto s1 = __builtin_amdgcn_permlane32_swap((unsigned)x1, (unsigned)y1, false, false);
-      const i32x4 out = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
-      const int dcol = 32 * dt + 16 * p + 8 * hi;
-      __builtin_amdgcn_raw_buffer_store_b128(out, ro, (uint32_t)qrow * row_bytes + dcol * 2, 0, 0);
-    }
+    if (grp == 0) wg_barrier();
+    store_block<D, F16>(O[0], m[0], l[0], c, wrow0, nq, row_bytes, ro, lse_row, lane);
   }
 }
 
-template <int D, int BR, int BC, int NW, int STAGES, bool F16>
+template <int D, int BR, int BC, int NW, int STAGES, bool F16, int SCHED>
 hipError_t launch_fa_fwd(const FaArgs &a, hipStream_t stream) {
   FaArgs arg = a;
   void *args[] = {&arg};
   // hipLaunchKernel reports this launch's own status (hipGetLastError would also return a
   // stale error left by some earlier, unrelated runtime call in this thread).
-  return hipLaunchKernel((const void *)&fa_fwd_kernel<D, BR, BC, NW, STAGES, F16>, dim3(a.total_wgs),
+  return hipLaunchKernel((const void *)&fa_fwd_kernel<D, BR, BC, NW, STAGES, F16, SCHED>, dim3(a.total_wgs),
                          dim3(NW * 64), args, 0, stream);
 }
 
-template <int D, int BR, int BC, int NW, int STAGES, bool F16>
+template <int D, int BR, int BC, int NW, int STAGES, bool F16, int SCHED = 0>
 KernelEntry make_entry() {
   KernelEntry e;
   e.dtype = F16 ? 1 : 0;
@@ -360,8 +676,9 @@ KernelEntry make_entry() {
   e.bc = BC;
   e.waves = NW;
   e.stages = STAGES;
-  e.launch = &launch_fa_fwd<D, BR, BC, NW, STAGES, F16>;
-  e.kernel = (const void *)&fa_fwd_kernel<D, BR, BC, NW, STAGES, F16>;
+  e.schedule = SCHED;
+  e.launch = &launch_fa_fwd<D, BR, BC, NW, STAGES, F16, SCHED>;
+  e.kernel = (const void *)&fa_fwd_kernel<D, BR, BC, NW, STAGES, F16, SCHED>;
   return e;
 }
 

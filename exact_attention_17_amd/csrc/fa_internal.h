@@ -30,7 +30,7 @@ typedef hipError_t (*LaunchFn)(const FaArgs &, hipStream_t);
 struct KernelEntry {
   int dtype;  // 0 bf16, 1 fp16
   int d_head;
-  int br, bc, waves, stages;
+  int br, bc, waves, stages, schedule;
   LaunchFn launch;
   const void *kernel;  // for hipFuncGetAttributes
 };

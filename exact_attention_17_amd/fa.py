@@ -27,13 +27,13 @@ class FaError(RuntimeError):
 
 class TileConfig(ctypes.Structure):
     _fields_ = [("br", ctypes.c_int), ("bc", ctypes.c_int), ("waves", ctypes.c_int),
-                ("stages", ctypes.c_int)]
+                ("stages", ctypes.c_int), ("schedule", ctypes.c_int)]
 
     def as_tuple(self):
-        return (self.br, self.bc, self.waves, self.stages)
+        return (self.br, self.bc, self.waves, self.stages, self.schedule)
 
     def __repr__(self):
-        return "TileConfig(br=%d, bc=%d, waves=%d, stages=%d)" % self.as_tuple()
+        return "TileConfig(br=%d, bc=%d, waves=%d, stages=%d, schedule=%d)" % self.as_tuple()
 
 
 _lib = None

@@ -62,16 +62,29 @@ typedef enum {
 
 /* A kernel tile configuration (page "Flash Attention 2 Chapter6", the
  * Kernel 7 configuration space: block rows B_r, block columns B_c, warps;
- * the buffering depth of the K/V stream).
- *   br     : query rows per workgroup (B_r)
- *   bc     : keys per K/V tile (B_c)
- *   waves  : 64-lane wavefronts per workgroup; each owns br / waves query rows
- *   stages : K/V tiles resident in LDS (1 = single buffer, 2 = double buffer) */
+ * the buffering depth of the K/V stream; the instruction schedule).
+ *   br       : query rows per workgroup (B_r)
+ *   bc       : keys per K/V tile (B_c)
+ *   waves    : 64-lane wavefronts per workgroup
+ *   stages   : K/V tile pairs resident in LDS (1 = single buffer, 2 = double
+ *              buffer, 3-4 = two or three tiles in flight while one is used)
+ *   schedule : 0 = each wavefront owns 32 query rows (br = 32 * waves) and runs
+ *                  QK^T, softmax and PV of a tile in turn;
+ *              1 = each wavefront owns 64 query rows (br = 64 * waves) as two
+ *                  32-row blocks whose softmax and matrix products are
+ *                  interleaved (one block's softmax runs while the other
+ *                  block's products issue; page "GPU 内核与 FlashAttention",
+ *                  sections 15.3-15.4); needs stages = 2;
+ *              2 = ping-pong: eight wavefronts of 32 rows in two groups that
+ *                  alternate, across a workgroup barrier, between the matrix
+ *                  products and the softmax (same page, section 15.3); needs
+ *                  waves = 8 and stages = 2 */
 typedef struct {
   int br;
   int bc;
   int waves;
   int stages;
+  int schedule;
 } fa_tile_config_t;
 
 /* The forward pass.  See the conventions above.  dtype is an fa_dtype_t.
@@ -98,8 +111,11 @@ int fa_fwd_autotune(const void *q, const void *k, const void *v, void *o, float 
                     fa_tile_config_t *chosen, float *best_ms);
 
 /* Force the configuration fa_fwd uses for (d_head, dtype); cfg == NULL
- * returns to automatic choice (tuned entry, else the built-in default).
- * FA_ERR_UNSUPPORTED if no kernel was compiled for cfg. */
+ * returns to automatic choice.  Automatic choice, in order: the environment
+ * variable FA_FWD_CONFIG="br,bc,waves,stages,schedule" (read once; applies
+ * to every (d_head, dtype) that has that configuration compiled), then a
+ * configuration fa_fwd_autotune chose for this shape class, then the
+ * built-in default.  FA_ERR_UNSUPPORTED if no kernel was compiled for cfg. */
 int fa_fwd_set_config(int d_head, int dtype, const fa_tile_config_t *cfg);
 
 /* The configuration fa_fwd would use for this shape (host-only lookup).
@@ -114,8 +130,9 @@ int fa_fwd_num_configs(int d_head, int dtype);
  * out; returns how many there are in total (< 0 on bad args).  Host-only. */
 int fa_fwd_list_configs(int d_head, int dtype, fa_tile_config_t *out, int capacity);
 
-/* LDS bytes a configuration uses per workgroup (stages x (K tile + V tile)),
- * from the configuration alone.  Host-only; < 0 on bad args. */
+/* LDS bytes a configuration uses per workgroup, from the configuration alone:
+ * stages x (K tile + V tile) for schedule 0, five tiles (two K, three V) for
+ * schedule 1; a tile is bc x d_head 16-bit values.  Host-only; < 0 on bad args. */
 int fa_fwd_config_lds_bytes(int d_head, const fa_tile_config_t *cfg);
 
 /* Register and spill figures the compiler reports for a compiled

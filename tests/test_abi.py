@@ -86,9 +86,18 @@ def test_config_registry_host_only():
             cfgs = fa.fa_fwd_list_configs(d, dtype)
             assert len(cfgs) == fa.fa_fwd_num_configs(d, dtype) >= 1
             for c in cfgs:
-                assert c.br == 32 * c.waves
-                assert c.stages in (1, 2)
-                assert fa.fa_fwd_config_lds_bytes(d, c) == c.stages * 2 * c.bc * d * 2
+                assert c.stages in (1, 2, 3, 4)
+                assert c.schedule in (0, 1, 2)
+                tile = c.bc * d * 2
+                if c.schedule == 1:
+                    assert c.br == 64 * c.waves and c.stages == 2
+                    assert fa.fa_fwd_config_lds_bytes(d, c) == 5 * tile
+                else:
+                    if c.schedule == 2:
+                        assert c.waves == 8 and c.stages == 2
+                    assert c.br == 32 * c.waves
+                    assert fa.fa_fwd_config_lds_bytes(d, c) == c.stages * 2 * tile
+                assert fa.fa_fwd_config_lds_bytes(d, c) <= 160 * 1024
     with pytest.raises(fa.FaError):
         fa.fa_fwd_num_configs(48, fa.FA_BF16)
     with pytest.raises(fa.FaError):
@@ -97,19 +106,19 @@ def test_config_registry_host_only():
 
 def test_default_and_forced_config():
     c = fa.fa_fwd_get_config(16, 4096, 4096, 16, 128, fa.FA_BF16)
-    assert c.as_tuple() == (128, 64, 4, 2)
+    assert c.as_tuple() == (256, 64, 8, 2, 0)
     small = fa.fa_fwd_get_config(1, 64, 4096, 1, 128, fa.FA_BF16)
     assert small.br == 64
     with pytest.raises(fa.FaError):
         fa.fa_fwd_set_config(128, fa.FA_BF16, (96, 64, 3, 2))  # not compiled
     fa.fa_fwd_set_config(128, fa.FA_BF16, (128, 32, 4, 2))
     try:
-        assert fa.fa_fwd_get_config(16, 4096, 4096, 16, 128, fa.FA_BF16).as_tuple() == (128, 32, 4, 2)
+        assert fa.fa_fwd_get_config(16, 4096, 4096, 16, 128, fa.FA_BF16).as_tuple() == (128, 32, 4, 2, 0)
         # forcing one (d, dtype) leaves the others alone
-        assert fa.fa_fwd_get_config(16, 4096, 4096, 16, 64, fa.FA_BF16).as_tuple() == (128, 64, 4, 2)
+        assert fa.fa_fwd_get_config(16, 4096, 4096, 16, 64, fa.FA_BF16).as_tuple() == (128, 64, 4, 2, 0)
     finally:
         fa.fa_fwd_set_config(128, fa.FA_BF16, None)
-    assert fa.fa_fwd_get_config(16, 4096, 4096, 16, 128, fa.FA_BF16).as_tuple() == (128, 64, 4, 2)
+    assert fa.fa_fwd_get_config(16, 4096, 4096, 16, 128, fa.FA_BF16).as_tuple() == (256, 64, 8, 2, 0)
 
 
 def test_autotune_rejects_bad_args_on_host():
