@@ -1,5 +1,5 @@
 /*
- * attn_oracle.c -- fp64 CPU oracle for exact (non-causal) attention.
+ * attn_oracle.c -- fp64 CPU oracle for exact attention.
  *
  * TEST INFRASTRUCTURE ONLY.  This file, and everything else under oracle/,
  * is the checker that the GPU path is compared against.  Only the tests,
@@ -24,11 +24,23 @@
  * shifted exponentials summed, and the output is the normalised weighted
  * sum of value rows.
  *
+ * Two options of the same page, section 14:
+ *  - causal (section 14.4): the score of key j for query i is -infinity when
+ *    j > i, indices counted from the start of the sequence (for Nq != Nk this
+ *    is the literal j > i, top-left aligned); exp(-inf) = 0, so row i is the
+ *    softmax over keys 0..i.  Key 0 is visible to every row, so m is finite.
+ *  - grouped K/V heads (section 14.2, MQA/GQA): k and v have heads_kv heads,
+ *    heads_kv divides heads, and query head h reads K/V head
+ *    h / (heads / heads_kv); nothing is copied.
+ *
  * oracle_attention_online() is the second function: the one-pass blockwise
  * recurrence of section 11.2 (two-block merge of (m, l)) and section 11.3
  * (running unnormalised output rescaled by exp(m - m'), divided by l at the
  * end), also in fp64.  It exists so that tests can show the recurrence the
- * GPU kernel relies on reaches the same result as the definition.
+ * GPU kernel relies on reaches the same result as the definition; with the
+ * causal option it also skips every key block lying wholly above the
+ * diagonal and masks inside the others (section 14.4), which must still
+ * give the definition's result.
  */
 #include <math.h>
 #ifdef _OPENMP
@@ -44,16 +56,19 @@ static inline int64_t at(int64_t row, int64_t head, int64_t t, int64_t heads, in
 }
 
 /* One query row of the definition.  qrow0/krow0 are the first token rows of
- * this sequence in the q and k/v arrays; i the query index in the sequence. */
+ * this sequence in the q and k/v arrays; i the query index in the sequence;
+ * h the query head and hk the K/V head it reads. */
 static void one_row(const double *q, const double *k, const double *v, double *o_row,
                     double *lse_out, int64_t qrow0, int64_t krow0, int64_t i, int64_t nk,
-                    int64_t h, int64_t heads, int64_t d, double scale, double *s) {
-  /* s_j = scale * <q_i, k_j> */
+                    int64_t h, int64_t hk, int64_t heads, int64_t heads_kv, int64_t d,
+                    double scale, int causal, double *s) {
+  /* s_j = scale * <q_i, k_j>; -inf above the diagonal when causal */
   for (int64_t j = 0; j < nk; ++j) {
     double acc = 0.0;
     for (int64_t t = 0; t < d; ++t)
-      acc += q[at(qrow0 + i, h, t, heads, d)] * k[at(krow0 + j, h, t, heads, d)];
+      acc += q[at(qrow0 + i, h, t, heads, d)] * k[at(krow0 + j, hk, t, heads_kv, d)];
     s[j] = scale * acc;
+    if (causal && j > i) s[j] = -INFINITY;
   }
   /* m = max_j s_j */
   double m = -INFINITY;
@@ -65,7 +80,7 @@ static void one_row(const double *q, const double *k, const double *v, double *o
   for (int64_t t = 0; t < d; ++t) o_row[t] = 0.0;
   for (int64_t j = 0; j < nk; ++j) {
     double p = exp(s[j] - m) / l;
-    for (int64_t t = 0; t < d; ++t) o_row[t] += p * v[at(krow0 + j, h, t, heads, d)];
+    for (int64_t t = 0; t < d; ++t) o_row[t] += p * v[at(krow0 + j, hk, t, heads_kv, d)];
   }
   *lse_out = m + log(l);
 }
@@ -73,15 +88,18 @@ static void one_row(const double *q, const double *k, const double *v, double *o
 /*
  * Full attention.
  *  q, o:   dense [batch, nq, heads, d]; varlen (cu != NULL) packed [cu[batch], heads, d]
- *  k, v:   dense [batch, nk, heads, d]; varlen packed [cu[batch], heads, d]
+ *  k, v:   dense [batch, nk, heads_kv, d]; varlen packed [cu[batch], heads_kv, d]
  *  lse:    [batch, heads, nq]  (varlen: nq is the row pitch, i.e. max length; rows past a
  *          sequence's length are left untouched)
  *  cu:     NULL for dense, else batch+1 non-decreasing prefix offsets shared by q and k.
- * Returns 0, or -1 if scratch memory could not be obtained.
+ *  causal: nonzero masks key j > query i (per sequence).
+ * Returns 0, -1 if scratch memory could not be obtained, -2 if heads_kv does not divide heads.
  */
 int oracle_attention(const double *q, const double *k, const double *v, double *o, double *lse,
-                     int64_t batch, int64_t nq, int64_t nk, int64_t heads, int64_t d,
-                     double scale, const int64_t *cu) {
+                     int64_t batch, int64_t nq, int64_t nk, int64_t heads, int64_t heads_kv,
+                     int64_t d, double scale, int causal, const int64_t *cu) {
+  if (heads_kv <= 0 || heads % heads_kv != 0) return -2;
+  const int64_t group = heads / heads_kv;
   int64_t max_nk = nk;
   if (cu) {
     max_nk = 0;
@@ -106,7 +124,7 @@ int oracle_attention(const double *q, const double *k, const double *v, double *
           int64_t qrow0 = cu ? cu[b] : b * nq;
           int64_t krow0 = cu ? cu[b] : b * nk;
           one_row(q, k, v, o + at(qrow0 + i, h, 0, heads, d), lse + (b * heads + h) * nq + i,
-                  qrow0, krow0, i, lk, h, heads, d, scale, s);
+                  qrow0, krow0, i, lk, h, h / group, heads, heads_kv, d, scale, causal, s);
         }
     free(s);
   }
@@ -119,9 +137,10 @@ int oracle_attention(const double *q, const double *k, const double *v, double *
  */
 int oracle_attention_rows(const double *q, const double *k, const double *v, double *o_rows,
                           double *lse_rows, int64_t batch, int64_t nq, int64_t nk, int64_t heads,
-                          int64_t d, double scale, const int64_t *cu, const int64_t *rows,
-                          int64_t n_rows) {
-  (void)batch;
+                          int64_t heads_kv, int64_t d, double scale, int causal,
+                          const int64_t *cu, const int64_t *rows, int64_t n_rows) {
+  if (heads_kv <= 0 || heads % heads_kv != 0) return -2;
+  const int64_t group = heads / heads_kv;
   int64_t max_nk = nk;
   if (cu) {
     max_nk = 0;
@@ -142,7 +161,8 @@ int oracle_attention_rows(const double *q, const double *k, const double *v, dou
       int64_t lk = cu ? cu[b + 1] - cu[b] : nk;
       int64_t qrow0 = cu ? cu[b] : b * nq;
       int64_t krow0 = cu ? cu[b] : b * nk;
-      one_row(q, k, v, o_rows + r * d, lse_rows + r, qrow0, krow0, i, lk, h, heads, d, scale, s);
+      one_row(q, k, v, o_rows + r * d, lse_rows + r, qrow0, krow0, i, lk, h, h / group, heads,
+              heads_kv, d, scale, causal, s);
     }
     free(s);
   }
@@ -150,16 +170,18 @@ int oracle_attention_rows(const double *q, const double *k, const double *v, dou
 }
 
 /*
- * The blockwise one-pass recurrence (dense layout only), block = key-block size.
- * State per query row: running max m (starts at -inf), running denominator l
+ * The blockwise one-pass recurrence (dense layout, heads_kv = heads), block = key-block
+ * size.  State per query row: running max m (starts at -inf), running denominator l
  * (starts at 0) and unnormalised output ot (starts at 0).  For each key block:
  * m' = max(m, max of the block's scores); l <- exp(m - m') l + sum exp(s - m');
  * ot <- exp(m - m') ot + sum exp(s - m') v; m <- m'.  At the end O = ot / l and
  * LSE = m + log l.  exp(m - m') with m = -inf is taken as 0 (nothing accumulated yet).
+ * Causal: a block whose first key is past i is skipped whole; inside the others a key
+ * past i scores -inf.
  */
 int oracle_attention_online(const double *q, const double *k, const double *v, double *o,
                             double *lse, int64_t batch, int64_t nq, int64_t nk, int64_t heads,
-                            int64_t d, double scale, int64_t block) {
+                            int64_t d, double scale, int causal, int64_t block) {
   if (block <= 0) return -1;
   int failed = 0;
 #pragma omp parallel
@@ -178,6 +200,7 @@ int oracle_attention_online(const double *q, const double *k, const double *v, d
           double m = -INFINITY, l = 0.0;
           for (int64_t t = 0; t < d; ++t) ot[t] = 0.0;
           for (int64_t j0 = 0; j0 < nk; j0 += block) {
+            if (causal && j0 > i) break; /* this block and every later one lie above the diagonal */
             int64_t nb = nk - j0 < block ? nk - j0 : block;
             double mb = -INFINITY;
             for (int64_t jj = 0; jj < nb; ++jj) {
@@ -185,6 +208,7 @@ int oracle_attention_online(const double *q, const double *k, const double *v, d
               for (int64_t t = 0; t < d; ++t)
                 acc += q[at(b * nq + i, h, t, heads, d)] * k[at(b * nk + j0 + jj, h, t, heads, d)];
               s[jj] = scale * acc;
+              if (causal && j0 + jj > i) s[jj] = -INFINITY;
               if (s[jj] > mb) mb = s[jj];
             }
             double mn = m > mb ? m : mb;

@@ -8,6 +8,9 @@ Definition followed (page "GPU 内核与 FlashAttention", sections 10, 11.1, 13.
 for each batch b, head h and query i,
     s_ij = scale * <q_i, k_j>,  m_i = max_j s_ij,  l_i = sum_j exp(s_ij - m_i),
     O_i  = sum_j exp(s_ij - m_i) / l_i * v_j,  LSE_i = m_i + ln l_i.
+Options of the same page's section 14: causal (s_ij = -inf for j > i, section 14.4)
+and grouped K/V heads (k, v with heads_kv heads; query head h reads K/V head
+h // (heads // heads_kv), section 14.2).  heads_kv is read off k's shape.
 """
 import ctypes
 import os
@@ -44,14 +47,14 @@ def build(force=True):
 def _bind(path):
     lib = ctypes.CDLL(path)
     lib.oracle_attention.restype = ctypes.c_int
-    lib.oracle_attention.argtypes = [_D, _D, _D, _D, _D, _i64, _i64, _i64, _i64, _i64,
-                                     ctypes.c_double, _I64]
+    lib.oracle_attention.argtypes = [_D, _D, _D, _D, _D, _i64, _i64, _i64, _i64, _i64, _i64,
+                                     ctypes.c_double, ctypes.c_int, _I64]
     lib.oracle_attention_rows.restype = ctypes.c_int
-    lib.oracle_attention_rows.argtypes = [_D, _D, _D, _D, _D, _i64, _i64, _i64, _i64, _i64,
-                                          ctypes.c_double, _I64, _I64, _i64]
+    lib.oracle_attention_rows.argtypes = [_D, _D, _D, _D, _D, _i64, _i64, _i64, _i64, _i64, _i64,
+                                          ctypes.c_double, ctypes.c_int, _I64, _I64, _i64]
     lib.oracle_attention_online.restype = ctypes.c_int
     lib.oracle_attention_online.argtypes = [_D, _D, _D, _D, _D, _i64, _i64, _i64, _i64, _i64,
-                                            ctypes.c_double, _i64]
+                                            ctypes.c_double, ctypes.c_int, _i64]
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
 
@@ -71,16 +74,19 @@ def _f64(a):
 
 
 def _shapes(q, k, v, cu_seqlens, max_seqlen):
+    """-> (batch, nq, nk, heads, heads_kv, d, cu)"""
     if cu_seqlens is None:
         if q.ndim != 4 or k.ndim != 4 or v.shape != k.shape:
             raise ValueError("dense q, k, v must be [B, N, H, D] with k and v alike")
         batch, nq, heads, d = q.shape
-        if k.shape[0] != batch or k.shape[2:] != (heads, d):
-            raise ValueError("q and k disagree on batch, heads or d")
-        return batch, nq, k.shape[1], heads, d, None
+        hkv = k.shape[2]
+        if k.shape[0] != batch or k.shape[3] != d or hkv < 1 or heads % hkv:
+            raise ValueError("q and k disagree on batch or d, or k's heads do not divide q's")
+        return batch, nq, k.shape[1], heads, hkv, d, None
     cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
-    if q.ndim != 3 or q.shape != k.shape or k.shape != v.shape:
-        raise ValueError("varlen q, k, v must all be [total, H, D]")
+    if q.ndim != 3 or k.ndim != 3 or k.shape != v.shape or q.shape[0] != k.shape[0] or \
+            q.shape[2] != k.shape[2] or k.shape[1] < 1 or q.shape[1] % k.shape[1]:
+        raise ValueError("varlen q must be [total, H, D] and k, v [total, Hkv, D] with Hkv | H")
     batch = cu.shape[0] - 1
     if cu[0] != 0 or np.any(np.diff(cu) < 0) or cu[-1] != q.shape[0]:
         raise ValueError("cu_seqlens must start at 0, not decrease, and end at total")
@@ -89,19 +95,20 @@ def _shapes(q, k, v, cu_seqlens, max_seqlen):
         max_seqlen = lmax
     if max_seqlen < lmax:
         raise ValueError("max_seqlen smaller than the longest sequence")
-    return batch, max_seqlen, max_seqlen, q.shape[1], q.shape[2], cu
+    return batch, max_seqlen, max_seqlen, q.shape[1], k.shape[1], q.shape[2], cu
 
 
-def attention(q, k, v, scale, cu_seqlens=None, max_seqlen=None, _lib_override=None):
+def attention(q, k, v, scale, cu_seqlens=None, max_seqlen=None, causal=False, _lib_override=None):
     """Exact attention in fp64.
 
-    Dense: q [B, Nq, H, D], k/v [B, Nk, H, D] -> (O [B, Nq, H, D], LSE [B, H, Nq]).
-    Varlen: q/k/v [total, H, D] with cu_seqlens [B+1] -> (O [total, H, D],
+    Dense: q [B, Nq, H, D], k/v [B, Nk, Hkv, D] -> (O [B, Nq, H, D], LSE [B, H, Nq]).
+    Varlen: q [total, H, D], k/v [total, Hkv, D] with cu_seqlens [B+1] -> (O [total, H, D],
     LSE [B, H, max_seqlen]); LSE rows past a sequence's length are NaN.
+    causal masks key j > query i (indices within the sequence).
     """
     lib = _lib_override or _load()
-    batch, nq, nk, heads, d, cu = _shapes(np.asarray(q), np.asarray(k), np.asarray(v),
-                                          cu_seqlens, max_seqlen)
+    batch, nq, nk, heads, hkv, d, cu = _shapes(np.asarray(q), np.asarray(k), np.asarray(v),
+                                               cu_seqlens, max_seqlen)
     q, qp = _f64(q)
     k, kp = _f64(k)
     v, vp = _f64(v)
@@ -109,17 +116,18 @@ def attention(q, k, v, scale, cu_seqlens=None, max_seqlen=None, _lib_override=No
     lse = np.full((batch, heads, nq), np.nan, dtype=np.float64)
     cup = cu.ctypes.data_as(_I64) if cu is not None else None
     rc = lib.oracle_attention(qp, kp, vp, o.ctypes.data_as(_D), lse.ctypes.data_as(_D),
-                              batch, nq, nk, heads, d, float(scale), cup)
+                              batch, nq, nk, heads, hkv, d, float(scale), int(bool(causal)), cup)
     if rc != 0:
         raise MemoryError("oracle_attention failed")
     return o, lse
 
 
-def attention_rows(q, k, v, scale, rows, cu_seqlens=None, max_seqlen=None, _lib_override=None):
+def attention_rows(q, k, v, scale, rows, cu_seqlens=None, max_seqlen=None, causal=False,
+                   _lib_override=None):
     """O and LSE for selected (b, h, i) rows only: returns (O [n, D], LSE [n])."""
     lib = _lib_override or _load()
-    batch, nq, nk, heads, d, cu = _shapes(np.asarray(q), np.asarray(k), np.asarray(v),
-                                          cu_seqlens, max_seqlen)
+    batch, nq, nk, heads, hkv, d, cu = _shapes(np.asarray(q), np.asarray(k), np.asarray(v),
+                                               cu_seqlens, max_seqlen)
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
     for b, h, i in rows:
         lq = (cu[b + 1] - cu[b]) if cu is not None else nq
@@ -133,24 +141,28 @@ def attention_rows(q, k, v, scale, rows, cu_seqlens=None, max_seqlen=None, _lib_
     lse = np.zeros((n,), dtype=np.float64)
     cup = cu.ctypes.data_as(_I64) if cu is not None else None
     rc = lib.oracle_attention_rows(qp, kp, vp, o.ctypes.data_as(_D), lse.ctypes.data_as(_D),
-                                   batch, nq, nk, heads, d, float(scale), cup,
-                                   rows.ctypes.data_as(_I64), n)
+                                   batch, nq, nk, heads, hkv, d, float(scale), int(bool(causal)),
+                                   cup, rows.ctypes.data_as(_I64), n)
     if rc != 0:
         raise MemoryError("oracle_attention_rows failed")
     return o, lse
 
 
-def attention_online(q, k, v, scale, block, _lib_override=None):
-    """The blockwise one-pass recurrence in fp64 (dense layout), key blocks of `block`."""
+def attention_online(q, k, v, scale, block, causal=False, _lib_override=None):
+    """The blockwise one-pass recurrence in fp64 (dense layout, as many K/V heads as query
+    heads), key blocks of `block`; with causal, blocks above the diagonal are skipped."""
     lib = _lib_override or _load()
-    batch, nq, nk, heads, d, _ = _shapes(np.asarray(q), np.asarray(k), np.asarray(v), None, None)
+    batch, nq, nk, heads, hkv, d, _ = _shapes(np.asarray(q), np.asarray(k), np.asarray(v), None, None)
+    if hkv != heads:
+        raise ValueError("attention_online takes as many K/V heads as query heads")
     q, qp = _f64(q)
     k, kp = _f64(k)
     v, vp = _f64(v)
     o = np.zeros(q.shape, dtype=np.float64)
     lse = np.zeros((batch, heads, nq), dtype=np.float64)
     rc = lib.oracle_attention_online(qp, kp, vp, o.ctypes.data_as(_D), lse.ctypes.data_as(_D),
-                                     batch, nq, nk, heads, d, float(scale), int(block))
+                                     batch, nq, nk, heads, d, float(scale), int(bool(causal)),
+                                     int(block))
     if rc != 0:
         raise ValueError("oracle_attention_online failed (block must be > 0)")
     return o, lse

@@ -5,7 +5,10 @@ real oracle and against deliberately altered builds of it.
 
 Sources: page "GPU 内核与 FlashAttention" section 10 (attention as S = QK^T with a
 1/sqrt(d)-type scale, softmax, PV), section 11.1 (safe softmax), sections 11.2-11.3
-(the blockwise recurrence is exact), section 13.2 (LSE = m + log l).
+(the blockwise recurrence is exact), section 13.2 (LSE = m + log l), section 14.2
+(grouped K/V heads: several query heads index one K/V head, nothing copied) and
+section 14.4 (causal: scores with j > i are -inf; blocks wholly above the diagonal can
+be skipped without changing the result).
 """
 import json
 import math
@@ -211,7 +214,127 @@ def pin_rows_match_full(orc):
         assert abs(lrow[n] - lse[b, h, i]) < 1e-14
 
 
+def pin_causal_hand_3x3(orc):
+    """q = k = I_3, v = [[0,1,2],[3,4,5],[6,7,8]], scale 1, causal.  Row i sees keys 0..i with
+    scores delta_ij: row 0 is v_0 with LSE 1; row 1 weighs (v_0, v_1) by (1, e)/(1+e) with
+    LSE ln(1+e); row 2 weighs (v_0, v_1, v_2) by (1, 1, e)/(2+e) with LSE ln(2+e)."""
+    e = math.e
+    eye = np.eye(3)
+    v = np.arange(9, dtype=np.float64).reshape(3, 3)
+    o, lse = orc.attention(_one_head(eye), _one_head(eye), _one_head(v), 1.0, causal=True)
+    want = [v[0], (v[0] + e * v[1]) / (1 + e), (v[0] + v[1] + e * v[2]) / (2 + e)]
+    np.testing.assert_allclose(o[0, :, 0, :], np.array(want), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0], [1.0, math.log(1 + e), math.log(2 + e)], rtol=0, atol=1e-12)
+
+
+def pin_causal_identical_keys(orc):
+    """All keys equal, causal: row i averages the values of keys 0..min(i, Nk-1) and its LSE
+    is s_i + ln(min(i+1, Nk)); rows past Nk (Nq > Nk) see every key."""
+    rng = np.random.default_rng(22)
+    nq, nk, d = 9, 6, 8
+    q = _rand(rng, 1, nq, 2, d)
+    k = np.broadcast_to(_rand(rng, 1, 1, 2, d), (1, nk, 2, d)).copy()
+    v = _rand(rng, 1, nk, 2, d)
+    o, lse = orc.attention(q, k, v, 0.4, causal=True)
+    for h in range(2):
+        for i in range(nq):
+            n = min(i + 1, nk)
+            np.testing.assert_allclose(o[0, i, h], v[0, :n, h].mean(axis=0), rtol=0, atol=1e-12)
+            s = 0.4 * float(q[0, i, h] @ k[0, 0, h])
+            assert abs(lse[0, h, i] - (s + math.log(n))) < 1e-12
+
+
+def pin_causal_value_identity(orc):
+    """Nk = d, V = I, causal: O_i is row i of the masked softmax, exactly 0 past column i,
+    and scipy's softmax / logsumexp of the first i+1 scores before it."""
+    rng = np.random.default_rng(23)
+    d = 12
+    q, k = _rand(rng, 1, d, 1, d), _rand(rng, 1, d, 1, d)
+    v = np.eye(d).reshape(1, d, 1, d)
+    o, lse = orc.attention(q, k, v, 0.5, causal=True)
+    s = 0.5 * (q[0, :, 0, :] @ k[0, :, 0, :].T)
+    for i in range(d):
+        assert np.all(o[0, i, 0, i + 1:] == 0.0)
+        np.testing.assert_allclose(o[0, i, 0, :i + 1], softmax(s[i, :i + 1]), rtol=0, atol=1e-13)
+        assert abs(lse[0, 0, i] - logsumexp(s[i, :i + 1])) < 1e-12
+
+
+def pin_causal_is_prefix_attention(orc):
+    """Causal row i equals unmasked attention of query i over keys 0..i alone (for Nq < Nk
+    and Nq > Nk alike)."""
+    rng = np.random.default_rng(24)
+    for nq, nk in ((7, 11), (11, 7)):
+        q, k, v = _rand(rng, 2, nq, 2, 8), _rand(rng, 2, nk, 2, 8), _rand(rng, 2, nk, 2, 8)
+        o, lse = orc.attention(q, k, v, 0.55, causal=True)
+        for i in range(nq):
+            n = min(i + 1, nk)
+            op, lsep = orc.attention(q[:, i:i + 1], k[:, :n], v[:, :n], 0.55)
+            np.testing.assert_allclose(o[:, i:i + 1], op, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[:, :, i:i + 1], lsep, rtol=0, atol=1e-12)
+
+
+def pin_causal_block_skipping_is_exact(orc):
+    """The blockwise recurrence that skips key blocks lying wholly above the diagonal and
+    masks inside the diagonal ones gives the masked definition's result, any block size."""
+    rng = np.random.default_rng(25)
+    q, k, v = _rand(rng, 1, 20, 2, 8, std=2.0), _rand(rng, 1, 20, 2, 8, std=2.0), _rand(rng, 1, 20, 2, 8)
+    o, lse = orc.attention(q, k, v, 0.6, causal=True)
+    for block in (1, 3, 8, 20, 64):
+        ob, lseb = orc.attention_online(q, k, v, 0.6, block, causal=True)
+        np.testing.assert_allclose(ob, o, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lseb, lse, rtol=0, atol=1e-12)
+
+
+def pin_causal_varlen_is_per_sequence(orc):
+    """Packed causal: every sequence's rows equal a dense causal call on that sequence."""
+    rng = np.random.default_rng(26)
+    lens = [6, 1, 13]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    total = int(cu[-1])
+    q, k, v = _rand(rng, total, 2, 8), _rand(rng, total, 2, 8), _rand(rng, total, 2, 8)
+    o, lse = orc.attention(q, k, v, 0.45, cu_seqlens=cu, causal=True)
+    for b, L in enumerate(lens):
+        sl = slice(cu[b], cu[b + 1])
+        od, lsed = orc.attention(q[None, sl], k[None, sl], v[None, sl], 0.45, causal=True)
+        np.testing.assert_allclose(o[sl], od[0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[b, :, :L], lsed[0], rtol=0, atol=1e-12)
+
+
+def pin_grouped_heads_are_repeated_heads(orc):
+    """Grouped K/V heads: with Hkv K/V heads, the result equals ordinary attention on K/V
+    with head h // (H / Hkv) copied into head h (MQA at Hkv = 1), dense and packed, plain and
+    causal; the selected-rows entry point agrees."""
+    rng = np.random.default_rng(27)
+    heads = 6
+    for hkv in (1, 2, 3):
+        g = heads // hkv
+        q = _rand(rng, 2, 9, heads, 8)
+        k, v = _rand(rng, 2, 13, hkv, 8), _rand(rng, 2, 13, hkv, 8)
+        krep, vrep = np.repeat(k, g, axis=2), np.repeat(v, g, axis=2)
+        for causal in (False, True):
+            o, lse = orc.attention(q, k, v, 0.5, causal=causal)
+            o2, lse2 = orc.attention(q, krep, vrep, 0.5, causal=causal)
+            np.testing.assert_allclose(o, o2, rtol=0, atol=1e-14)
+            np.testing.assert_allclose(lse, lse2, rtol=0, atol=1e-14)
+            rows = [(0, heads - 1, 8), (1, 1, 3), (1, g % heads, 0)]
+            orow, lrow = orc.attention_rows(q, k, v, 0.5, rows, causal=causal)
+            for n, (b, h, i) in enumerate(rows):
+                np.testing.assert_allclose(orow[n], o[b, i, h], rtol=0, atol=1e-14)
+                assert abs(lrow[n] - lse[b, h, i]) < 1e-14
+    lens = [4, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q = _rand(rng, 13, heads, 8)
+    k, v = _rand(rng, 13, 2, 8), _rand(rng, 13, 2, 8)
+    o, lse = orc.attention(q, k, v, 0.5, cu_seqlens=cu)
+    o2, lse2 = orc.attention(q, np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1), 0.5, cu_seqlens=cu)
+    np.testing.assert_allclose(o, o2, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, lse2, rtol=0, atol=1e-14, equal_nan=True)
+
+
 PINS = [pin_hand_2x2, pin_hand_4x4, pin_values_one, pin_identical_keys, pin_dominant_logit,
         pin_value_identity_is_softmax, pin_single_key, pin_permutations_and_linearity,
         pin_shift_invariance, pin_large_logits, pin_online_recurrence_is_exact,
-        pin_varlen_is_per_sequence, pin_rows_match_full]
+        pin_varlen_is_per_sequence, pin_rows_match_full, pin_causal_hand_3x3,
+        pin_causal_identical_keys, pin_causal_value_identity, pin_causal_is_prefix_attention,
+        pin_causal_block_skipping_is_exact, pin_causal_varlen_is_per_sequence,
+        pin_grouped_heads_are_repeated_heads]

@@ -20,18 +20,24 @@ def test_pin(pin, oracle_mod):
 MUTATIONS = {
     "scale_dropped": ("s[j] = scale * acc;", "s[j] = acc;"),
     "exp_sign_flipped": ("l += exp(s[j] - m);", "l += exp(m - s[j]);"),
-    "scores_wrong_index": ("acc += q[at(qrow0 + i, h, t, heads, d)] * k[at(krow0 + j, h, t, heads, d)];",
+    "scores_wrong_index": ("acc += q[at(qrow0 + i, h, t, heads, d)] * k[at(krow0 + j, hk, t, heads_kv, d)];",
                           "acc += q[at(qrow0 + (j % (nk < 1 ? 1 : nk)) % (i + 1), h, t, heads, d)]"
-                          " * k[at(krow0 + (i % nk), h, t, heads, d)];"),
+                          " * k[at(krow0 + (i % nk), hk, t, heads_kv, d)];"),
     "no_normalisation": ("double p = exp(s[j] - m) / l;", "double p = exp(s[j] - m);"),
     "lse_without_max": ("*lse_out = m + log(l);", "*lse_out = log(l);"),
     "no_max_shift": ("l += exp(s[j] - m);", "l += exp(s[j]);"),
-    "value_row_of_query": ("o_row[t] += p * v[at(krow0 + j, h, t, heads, d)];",
-                           "o_row[t] += p * v[at(krow0 + (i % nk), h, t, heads, d)];"),
+    "value_row_of_query": ("o_row[t] += p * v[at(krow0 + j, hk, t, heads_kv, d)];",
+                           "o_row[t] += p * v[at(krow0 + (i % nk), hk, t, heads_kv, d)];"),
     "max_is_min": ("if (s[j] > m) m = s[j];", "if (m == -INFINITY || s[j] < m) m = s[j];"),
     "online_no_rescale": ("for (int64_t t = 0; t < d; ++t) ot[t] *= alpha;", ""),
     "varlen_ignores_offsets": ("int64_t krow0 = cu ? cu[b] : b * nk;\n          one_row(",
                                "int64_t krow0 = cu ? 0 : b * nk;\n          one_row("),
+    "causal_ignored": ("if (causal && j > i) s[j] = -INFINITY;", ""),
+    "causal_off_by_one": ("if (causal && j > i) s[j] = -INFINITY;", "if (causal && j >= i) s[j] = -INFINITY;"),
+    "causal_masks_lower": ("if (causal && j > i) s[j] = -INFINITY;", "if (causal && j < i) s[j] = -INFINITY;"),
+    "causal_skips_diagonal_block": ("if (causal && j0 > i) break;", "if (causal && j0 + block > i + 1) break;"),
+    "causal_online_no_inner_mask": ("if (causal && j0 + jj > i) s[jj] = -INFINITY;", ""),
+    "grouped_head_modulo": ("h / group", "h % heads_kv"),
 }
 
 
