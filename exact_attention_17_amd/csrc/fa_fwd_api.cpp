@@ -73,8 +73,8 @@ bool valid_d(int d) { return d == 32 || d == 64 || d == 128; }
 // ------------------------------------------------------ configuration choice
 std::mutex g_cfg_mu;
 std::map<std::pair<int, int>, fa_tile_config_t> g_forced;  // (d, dtype) -> config
-// (d, dtype, varlen, ceil(log2(seqlen_q))) -> tuned config
-std::map<std::tuple<int, int, int, int>, fa_tile_config_t> g_tuned;
+// (d, dtype, varlen, causal, ceil(log2(seqlen_q))) -> tuned config
+std::map<std::tuple<int, int, int, int, int>, fa_tile_config_t> g_tuned;
 
 int log2_bucket(int n) {
   int b = 0;
@@ -106,26 +106,29 @@ const fa_tile_config_t *env_config() {
   return have ? &cfg : nullptr;
 }
 
-fa_tile_config_t choose_config(int seqlen_q, int d, int dtype, bool varlen) {
+fa_tile_config_t choose_config(int seqlen_q, int d, int dtype, bool varlen, bool causal) {
   const fa_tile_config_t *env = env_config();
   std::lock_guard<std::mutex> lk(g_cfg_mu);
   auto f = g_forced.find({d, dtype});
   if (f != g_forced.end()) return f->second;
   if (env && find_entry(dtype, d, *env)) return *env;
-  auto t = g_tuned.find({d, dtype, varlen ? 1 : 0, log2_bucket(seqlen_q)});
+  auto t = g_tuned.find({d, dtype, varlen ? 1 : 0, causal ? 1 : 0, log2_bucket(seqlen_q)});
   if (t != g_tuned.end()) return t->second;
   return default_config(seqlen_q, d);
 }
 
 // ------------------------------------------------------------ arg checks
 int check_args(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
-               int seqlen_q, int seqlen_k, int n_heads, int d_head, float scale,
-               const int32_t *cu_seqlens, int dtype) {
+               int seqlen_q, int seqlen_k, int n_heads, int n_heads_kv, int d_head, float scale,
+               int causal, const int32_t *cu_seqlens, int dtype) {
   if (!q || !k || !v || !o || !lse)
     return fail(FA_ERR_INVALID_ARG, "q, k, v, o and lse must be non-null device pointers");
   if (!valid_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "dtype must be FA_BF16 (0) or FA_FP16 (1)");
   if (batch < 1 || n_heads < 1 || seqlen_q < 1 || seqlen_k < 1)
     return fail(FA_ERR_INVALID_ARG, "batch, n_heads, seqlen_q and seqlen_k must be >= 1");
+  if (n_heads_kv < 1 || n_heads % n_heads_kv != 0)
+    return fail(FA_ERR_INVALID_ARG, "n_heads_kv must be >= 1 and divide n_heads");
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (!valid_d(d_head)) return fail(FA_ERR_UNSUPPORTED, "d_head must be 32, 64 or 128");
@@ -136,19 +139,20 @@ int check_args(const void *q, const void *k, const void *v, void *o, float *lse,
     return fail(FA_ERR_MISALIGNED, "q, k, v and o must be 16-byte aligned");
   if (mis(lse, 4)) return fail(FA_ERR_MISALIGNED, "lse must be 4-byte aligned");
   // Per-sequence byte offsets are 32-bit in the kernel (buffer addressing); one tile of
-  // slack past the longest sequence.
+  // slack past the longest sequence.  The fp32 split partials of one (split, batch, head)
+  // hold seqlen_q x d_head x 4 bytes.
   const int64_t row_bytes = (int64_t)n_heads * d_head * 2;
   const int64_t longest = std::max(seqlen_q, seqlen_k);
   if ((longest + 256) * row_bytes >= (int64_t)INT32_MAX)
     return fail(FA_ERR_UNSUPPORTED, "sequence length x n_heads x d_head too large for 32-bit offsets");
-  const int64_t wgs = (int64_t)batch * n_heads * ((seqlen_q + 63) / 64);
+  const int64_t wgs = (int64_t)batch * n_heads * ((seqlen_q + 63) / 64) * FA_MAX_SPLITS;
   if (wgs >= (int64_t)INT32_MAX) return fail(FA_ERR_UNSUPPORTED, "grid too large");
   return FA_OK;
 }
 
 FaArgs make_args(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
-                 int seqlen_q, int seqlen_k, int n_heads, float scale, const int32_t *cu_seqlens,
-                 int br) {
+                 int seqlen_q, int seqlen_k, int n_heads, int n_heads_kv, float scale, int causal,
+                 const int32_t *cu_seqlens, int br, int num_splits, float *o_part, float *lse_part) {
   FaArgs a;
   a.q = q;
   a.k = k;
@@ -160,19 +164,91 @@ FaArgs make_args(const void *q, const void *k, const void *v, void *o, float *ls
   a.seqlen_q = seqlen_q;
   a.seqlen_k = seqlen_k;
   a.heads = n_heads;
+  a.heads_kv = n_heads_kv;
+  a.group = n_heads / n_heads_kv;
+  a.causal = causal;
+  a.num_splits = num_splits;
   a.n_qtiles = (seqlen_q + br - 1) / br;
-  a.total_wgs = batch * n_heads * a.n_qtiles;
+  a.total_wgs = batch * n_heads * a.n_qtiles * num_splits;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
+  a.o_part = o_part;
+  a.lse_part = lse_part;
   return a;
 }
 
-int launch_entry(const KernelEntry &e, const void *q, const void *k, const void *v, void *o,
-                 float *lse, int batch, int seqlen_q, int seqlen_k, int n_heads, float scale,
-                 const int32_t *cu_seqlens, void *stream) {
-  const FaArgs a = make_args(q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, scale, cu_seqlens, e.br);
-  hipError_t err = e.launch(a, reinterpret_cast<hipStream_t>(stream));
+// One forward call on a resolved configuration and split count.  Split mode puts the fp32
+// partial outputs at the start of the workspace and their LSE rows after them.
+struct Call {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  int batch, seqlen_q, seqlen_k, n_heads, n_heads_kv, d_head;
+  float scale;
+  int causal;
+  const int32_t *cu_seqlens;
+  int dtype;
+  void *stream;
+};
+
+size_t workspace_bytes_of(int batch, int seqlen_q, int n_heads, int d_head, int num_splits) {
+  if (num_splits <= 1) return 0;
+  return (size_t)num_splits * (size_t)batch * (size_t)n_heads * (size_t)seqlen_q * (size_t)(d_head + 1) * 4u;
+}
+
+int launch_entry(const KernelEntry &e, const Call &c, int num_splits, void *workspace) {
+  float *o_part = nullptr, *lse_part = nullptr;
+  if (num_splits > 1) {
+    o_part = static_cast<float *>(workspace);
+    lse_part = o_part + (size_t)num_splits * c.batch * c.n_heads * c.seqlen_q * c.d_head;
+  }
+  const FaArgs a = make_args(c.q, c.k, c.v, c.o, c.lse, c.batch, c.seqlen_q, c.seqlen_k, c.n_heads,
+                             c.n_heads_kv, c.scale, c.causal, c.cu_seqlens, e.br, num_splits, o_part,
+                             lse_part);
+  hipStream_t s = reinterpret_cast<hipStream_t>(c.stream);
+  hipError_t err = e.launch(a, s);
   if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(err));
+  if (num_splits > 1) {
+    fa::MergeArgs m;
+    m.o_part = o_part;
+    m.lse_part = lse_part;
+    m.o = c.o;
+    m.lse = c.lse;
+    m.cu_seqlens = c.cu_seqlens;
+    m.batch = c.batch;
+    m.seqlen_q = c.seqlen_q;
+    m.heads = c.n_heads;
+    m.num_splits = num_splits;
+    err = fa::launch_merge(m, c.d_head, c.dtype, s);
+    if (err != hipSuccess)
+      return fail(FA_ERR_HIP, std::string("merge kernel launch failed: ") + hipGetErrorString(err));
+  }
   return ok();
+}
+
+int launch_entry(const KernelEntry &e, const Call &c) { return launch_entry(e, c, 1, nullptr); }
+
+Call make_call(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int seqlen_q,
+               int seqlen_k, int n_heads, int n_heads_kv, int d_head, float scale, int causal,
+               const int32_t *cu_seqlens, int dtype, void *stream) {
+  return Call{q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, n_heads_kv, d_head, scale, causal,
+              cu_seqlens, dtype, stream};
+}
+
+constexpr int kNumCUs = 256;
+
+// Splits for about two workgroups per CU when the grid alone is smaller than the CU count;
+// each split keeps at least two key tiles.
+int choose_splits(int batch, int seqlen_q, int seqlen_k, int n_heads, int d_head, int dtype, bool causal,
+                  bool varlen) {
+  const fa_tile_config_t c = choose_config(seqlen_q, d_head, dtype, varlen, causal);
+  const int64_t wgs = (int64_t)batch * n_heads * ((seqlen_q + c.br - 1) / c.br);
+  if (wgs >= kNumCUs) return 1;
+  const int64_t keys = causal ? std::min(seqlen_k, seqlen_q) : seqlen_k;
+  const int64_t nkt = (keys + c.bc - 1) / c.bc;
+  int64_t s = (2 * kNumCUs + wgs - 1) / wgs;
+  s = std::min<int64_t>(s, nkt / 2);
+  s = std::min<int64_t>(s, FA_MAX_SPLITS);
+  return (int)std::max<int64_t>(s, 1);
 }
 
 constexpr int kLdsLimit = 160 * 1024;
@@ -188,15 +264,65 @@ int lds_bytes_of(int d, const fa_tile_config_t &c) {
 
 extern "C" {
 
+int fa_fwd_ext(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int seqlen_q,
+               int seqlen_k, int n_heads, int n_heads_kv, int d_head, float scale, int causal,
+               const int32_t *cu_seqlens, int dtype, int num_splits, void *workspace, size_t workspace_bytes,
+               void *stream) {
+  int st = check_args(q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, n_heads_kv, d_head, scale, causal,
+                      cu_seqlens, dtype);
+  if (st != FA_OK) return st;
+  if (num_splits < 0 || num_splits > FA_MAX_SPLITS)
+    return fail(FA_ERR_INVALID_ARG, "num_splits must be 0 (automatic) or 1 .. FA_MAX_SPLITS");
+  const bool varlen = cu_seqlens != nullptr;
+  if (num_splits == 0) {
+    num_splits = choose_splits(batch, seqlen_q, seqlen_k, n_heads, d_head, dtype, causal != 0, varlen);
+    while (num_splits > 1 &&
+           (!workspace || workspace_bytes_of(batch, seqlen_q, n_heads, d_head, num_splits) > workspace_bytes))
+      --num_splits;
+  }
+  if (num_splits > 1) {
+    if (!workspace) return fail(FA_ERR_INVALID_ARG, "num_splits > 1 needs a workspace");
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+      return fail(FA_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+    if (workspace_bytes < workspace_bytes_of(batch, seqlen_q, n_heads, d_head, num_splits))
+      return fail(FA_ERR_INVALID_ARG, "workspace smaller than fa_fwd_workspace_bytes() for num_splits");
+  }
+  const fa_tile_config_t c = choose_config(seqlen_q, d_head, dtype, varlen, causal != 0);
+  const KernelEntry *e = find_entry(dtype, d_head, c);
+  if (!e) return fail(FA_ERR_UNSUPPORTED, "no compiled kernel for the chosen tile configuration");
+  const Call call = make_call(q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, n_heads_kv, d_head, scale,
+                              causal, cu_seqlens, dtype, stream);
+  return launch_entry(*e, call, num_splits, workspace);
+}
+
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int seqlen_q,
            int seqlen_k, int n_heads, int d_head, float scale, const int32_t *cu_seqlens, int dtype,
            void *stream) {
-  int st = check_args(q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, d_head, scale, cu_seqlens, dtype);
-  if (st != FA_OK) return st;
-  const fa_tile_config_t c = choose_config(seqlen_q, d_head, dtype, cu_seqlens != nullptr);
-  const KernelEntry *e = find_entry(dtype, d_head, c);
-  if (!e) return fail(FA_ERR_UNSUPPORTED, "no compiled kernel for the chosen tile configuration");
-  return launch_entry(*e, q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, scale, cu_seqlens, stream);
+  return fa_fwd_ext(q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, n_heads, d_head, scale, 0, cu_seqlens,
+                    dtype, 1, nullptr, 0, stream);
+}
+
+size_t fa_fwd_workspace_bytes(int batch, int seqlen_q, int n_heads, int d_head, int num_splits) {
+  if (batch < 1 || seqlen_q < 1 || n_heads < 1 || num_splits < 1 || num_splits > FA_MAX_SPLITS) {
+    fail(FA_ERR_INVALID_ARG, "batch, seqlen_q, n_heads must be >= 1 and num_splits in 1 .. FA_MAX_SPLITS");
+    return 0;
+  }
+  if (!valid_d(d_head)) {
+    fail(FA_ERR_UNSUPPORTED, "d_head must be 32, 64 or 128");
+    return 0;
+  }
+  ok();
+  return workspace_bytes_of(batch, seqlen_q, n_heads, d_head, num_splits);
+}
+
+int fa_fwd_choose_splits(int batch, int seqlen_q, int seqlen_k, int n_heads, int d_head, int dtype, int causal,
+                         int varlen) {
+  if (!valid_dtype(dtype)) return fail(-FA_ERR_INVALID_ARG, "dtype must be FA_BF16 (0) or FA_FP16 (1)");
+  if (batch < 1 || n_heads < 1 || seqlen_q < 1 || seqlen_k < 1)
+    return fail(-FA_ERR_INVALID_ARG, "batch, n_heads, seqlen_q and seqlen_k must be >= 1");
+  if (!valid_d(d_head)) return fail(-FA_ERR_UNSUPPORTED, "d_head must be 32, 64 or 128");
+  ok();
+  return choose_splits(batch, seqlen_q, seqlen_k, n_heads, d_head, dtype, causal != 0, varlen != 0);
 }
 
 int fa_fwd_set_config(int d_head, int dtype, const fa_tile_config_t *cfg) {
@@ -220,7 +346,7 @@ int fa_fwd_get_config(int batch, int seqlen_q, int seqlen_k, int n_heads, int d_
   if (batch < 1 || n_heads < 1 || seqlen_q < 1 || seqlen_k < 1)
     return fail(FA_ERR_INVALID_ARG, "batch, n_heads, seqlen_q and seqlen_k must be >= 1");
   if (!valid_d(d_head)) return fail(FA_ERR_UNSUPPORTED, "d_head must be 32, 64 or 128");
-  *out = choose_config(seqlen_q, d_head, dtype, varlen != 0);
+  *out = choose_config(seqlen_q, d_head, dtype, varlen != 0, false);
   return ok();
 }
 
@@ -275,9 +401,12 @@ int fa_fwd_autotune(const void *q, const void *k, const void *v, void *o, float 
                     int seqlen_q, int seqlen_k, int n_heads, int d_head, float scale,
                     const int32_t *cu_seqlens, int dtype, void *stream, int reps,
                     fa_tile_config_t *chosen, float *best_ms) {
-  int st = check_args(q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, d_head, scale, cu_seqlens, dtype);
+  int st = check_args(q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, n_heads, d_head, scale, 0, cu_seqlens,
+                      dtype);
   if (st != FA_OK) return st;
   if (reps < 1) return fail(FA_ERR_INVALID_ARG, "reps must be >= 1");
+  const Call call = make_call(q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, n_heads, d_head, scale, 0,
+                              cu_seqlens, dtype, stream);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipEvent_t e0 = nullptr, e1 = nullptr;
   auto cleanup = [&] {
@@ -297,14 +426,14 @@ int fa_fwd_autotune(const void *q, const void *k, const void *v, void *o, float 
     hipFuncAttributes attr;
     if (hipFuncGetAttributes(&attr, e.kernel) != hipSuccess) continue;
     if (attr.localSizeBytes > 0) continue;  // spills registers
-    int rc = launch_entry(e, q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, scale, cu_seqlens, stream);
+    int rc = launch_entry(e, call);
     if (rc != FA_OK) {
       cleanup();
       return rc;
     }
     if (hipEventRecord(e0, s) != hipSuccess) break;
     for (int r = 0; r < reps; ++r)
-      (void)launch_entry(e, q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, scale, cu_seqlens, stream);
+      (void)launch_entry(e, call);
     if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) {
       cleanup();
       return fail(FA_ERR_HIP, "event timing failed");
@@ -324,10 +453,10 @@ int fa_fwd_autotune(const void *q, const void *k, const void *v, void *o, float 
   if (!best) return fail(FA_ERR_UNSUPPORTED, "no configuration passed the LDS / spill filter");
   {
     std::lock_guard<std::mutex> lk(g_cfg_mu);
-    g_tuned[{d_head, dtype, cu_seqlens ? 1 : 0, log2_bucket(seqlen_q)}] = cfg_of(*best);
+    g_tuned[{d_head, dtype, cu_seqlens ? 1 : 0, 0, log2_bucket(seqlen_q)}] = cfg_of(*best);
   }
   // Leave O and LSE holding the winner's result.
-  int rc = launch_entry(*best, q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, scale, cu_seqlens, stream);
+  int rc = launch_entry(*best, call);
   if (rc != FA_OK) return rc;
   if (hipStreamSynchronize(s) != hipSuccess) return fail(FA_ERR_HIP, "hipStreamSynchronize failed");
   if (chosen) *chosen = cfg_of(*best);
@@ -337,6 +466,6 @@ int fa_fwd_autotune(const void *q, const void *k, const void *v, void *o, float 
 
 const char *fa_last_error(void) { return g_last_error.c_str(); }
 
-const char *fa_version(void) { return "fa_fwd 0.1 (gfx950)"; }
+const char *fa_version(void) { return "fa_fwd 0.2 (gfx950)"; }
 
 }  // extern "C"

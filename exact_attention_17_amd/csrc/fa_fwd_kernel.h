@@ -70,6 +70,7 @@ namespace fa {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -312,12 +313,15 @@ __device__ __forceinline__ float softmax_block(f32x16 (&S)[BC / 32], i32x4 (&P)[
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
   mx = pair_max(mx);
-  const bool grow = (mx - m) * c > kLazyRescale;  // always true on the first tile (m = -inf)
+  const bool grow = (mx - m) * c > kLazyRescale;  // true at the first visible key (m = -inf)
   const float m_new = grow ? mx : m;
-  const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);  // 0 on the first tile, else <= 1
+  // m_new stays -inf while a row has seen no visible key (a split of the key range that lies
+  // wholly above the diagonal for it); the exponentials are then taken against 0 and are 0.
+  const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f((m - m_ref) * c);  // 0 on the first tile, else <= 1
   rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
   m = m_new;
-  const float mc = m * c;
+  const float mc = m_ref * c;
   float rs = 0.f;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
@@ -381,6 +385,34 @@ __device__ __forceinline__ void store_block(const f32x16 (&O)[D / 32], float m, 
   }
 }
 
+// Split-mode finish of one 32-query block: the split's own normalised output in fp32 and its
+// natural-log LSE, or 0 and -inf for a row that saw no visible key.  rp covers this (split,
+// batch, head)'s [rows < nq, D] fp32 slab; lane l holds d = 32 dt + 8 g + 4 (l/32) + 0..3 of
+// row l % 32, four consecutive floats, stored as they are.
+template <int D>
+__device__ __forceinline__ void store_block_part(const f32x16 (&O)[D / 32], float m, float l, float c,
+                                                 int qrow0, int nq, const __amdgpu_buffer_rsrc_t &rp,
+                                                 float *lse_row, int lane) {
+  constexpr int DT = D / 32;
+  const int hi = lane >> 5;
+  l = pair_sum(l);
+  const bool seen = l > 0.f;
+  const float inv = seen ? 1.f / l : 0.f;
+  const int qrow = qrow0 + (lane & 31);
+  if (hi == 0 && qrow < nq)
+    lse_row[qrow] = seen ? 0.69314718055994531f * __builtin_fmaf(m, c, __builtin_amdgcn_logf(l)) : -INFINITY;
+  const uint32_t off = (uint32_t)qrow * (D * 4) + hi * 16;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 val = {O[dt][4 * g] * inv, O[dt][4 * g + 1] * inv, O[dt][4 * g + 2] * inv,
+                         O[dt][4 * g + 3] * inv};
+      // rows past nq are out of the buffer's range: the store is dropped
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, val), rp, off + (32 * dt + 8 * g) * 4, 0, 0);
+    }
+}
+
 template <int SCHED>
 constexpr int waves_per_simd() {
   return SCHED == 1 ? 1 : 2;
@@ -423,15 +455,21 @@ fa_fwd_kernel(FaArgs a) {
   const int hi = lane >> 5;  // which half of the wavefront
 
   // Renumber workgroups: hardware deals consecutive ids round-robin over the 8 XCDs,
-  // so give XCD x a contiguous range of (batch, head, q-tile) work items.
+  // so give XCD x a contiguous range of (batch, head, q-tile, split) work items.
   const int w = blockIdx.x;
   const int G = a.total_wgs;
   const int per = G >> 3, rem = G & 7, xcd = w & 7;
   const int lin = xcd * per + min(xcd, rem) + (w >> 3);
-  const int qt = lin % a.n_qtiles;
-  const int bh = lin / a.n_qtiles;
+  const int nsplit = a.num_splits;
+  const int split = lin % nsplit;
+  const int lt = lin / nsplit;
+  const int qi = lt % a.n_qtiles;
+  // under the causal mask the work of a query tile grows with its index: start the longest
+  const int qt = a.causal ? a.n_qtiles - 1 - qi : qi;
+  const int bh = lt / a.n_qtiles;
   const int h = bh % a.heads;
   const int b = bh / a.heads;
+  const int hk = h / a.group;  // the K/V head this query head reads
 
   int nq, nk;
   int64_t qrow0, krow0;
@@ -449,17 +487,32 @@ fa_fwd_kernel(FaArgs a) {
   if (q_tile0 >= nq || nk <= 0) return;  // uniform over the workgroup
 
   const int64_t hd = (int64_t)a.heads * D;
+  const int64_t hkd = (int64_t)a.heads_kv * D;
   const uint32_t row_bytes = (uint32_t)(hd * 2);
-  const int64_t head_off = (int64_t)h * D;
-  const char *qb = (const char *)a.q + (qrow0 * hd + head_off) * 2;
-  const char *kb_ = (const char *)a.k + (krow0 * hd + head_off) * 2;
-  const char *vb = (const char *)a.v + (krow0 * hd + head_off) * 2;
-  char *ob = (char *)a.o + (qrow0 * hd + head_off) * 2;
+  const uint32_t kv_row_bytes = (uint32_t)(hkd * 2);
+  const char *qb = (const char *)a.q + (qrow0 * hd + (int64_t)h * D) * 2;
+  const char *kb_ = (const char *)a.k + (krow0 * hkd + (int64_t)hk * D) * 2;
+  const char *vb = (const char *)a.v + (krow0 * hkd + (int64_t)hk * D) * 2;
+  char *ob = (char *)a.o + (qrow0 * hd + (int64_t)h * D) * 2;
   const auto rq = make_rsrc(qb, (uint32_t)(nq - 1) * row_bytes + ROWB);
-  const auto rk = make_rsrc(kb_, (uint32_t)(nk - 1) * row_bytes + ROWB);
-  const auto rv = make_rsrc(vb, (uint32_t)(nk - 1) * row_bytes + ROWB);
+  const auto rk = make_rsrc(kb_, (uint32_t)(nk - 1) * kv_row_bytes + ROWB);
+  const auto rv = make_rsrc(vb, (uint32_t)(nk - 1) * kv_row_bytes + ROWB);
   const auto ro = make_rsrc(ob, (uint32_t)(nq - 1) * row_bytes + ROWB);
-  float *lse_row = a.lse + ((int64_t)b * a.heads + h) * a.seqlen_q;
+  const int64_t lse_base = ((int64_t)b * a.heads + h) * a.seqlen_q;
+  float *lse_row = a.lse + lse_base;
+  // split mode: this split's fp32 slab [rows < nq, D] and its LSE row
+  const int64_t part_base = (int64_t)split * a.batch * a.heads * a.seqlen_q + lse_base;
+  float *lse_part_row = a.lse_part + part_base;
+  const auto rp = make_rsrc(a.o_part + part_base * D, (uint32_t)nq * (D * 4));
+
+  // Key tiles this workgroup visits: [0, nk), or under the causal mask those up to the
+  // tile's last query row (the rest lie wholly above the diagonal and are skipped); split
+  // `split` of nsplit takes tiles [jb, je) of them.
+  const int kend = a.causal ? min(nk, q_tile0 + BR) : nk;
+  const int nkt_all = (kend + BC - 1) / BC;
+  const int jb = (int)((int64_t)nkt_all * split / nsplit);
+  const int je = (int)((int64_t)nkt_all * (split + 1) / nsplit);
+  const int ntl = je - jb;  // may be 0: the split then reports "no visible key"
 
   // Q stays in registers as the B operand (16 d per step) of each 32-row block.
   const int wrow0 = q_tile0 + wave * QW;  // first row of this wavefront
@@ -478,7 +531,7 @@ fa_fwd_kernel(FaArgs a) {
   auto load_by = [&](const __amdgpu_buffer_rsrc_t &rsrc, char *dst, int j, int lw, auto lw_c)
                      __attribute__((always_inline)) {
     constexpr int LW = decltype(lw_c)::value;
-    const uint32_t tile_off = (uint32_t)(j * BC) * row_bytes;
+    const uint32_t tile_off = (uint32_t)(j * BC) * kv_row_bytes;
 #pragma unroll
     for (int i = 0; i < (NCH + LW - 1) / LW; ++i) {
       const int u = lw + i * LW;
@@ -486,7 +539,7 @@ fa_fwd_kernel(FaArgs a) {
         const int pos = u * 1024 + lane * 16;
         const int r = pos / ROWB;
         const int cc = ((pos % ROWB) >> 4) ^ swz<D>(r);
-        const uint32_t goff = tile_off + (uint32_t)r * row_bytes + cc * 16;
+        const uint32_t goff = tile_off + (uint32_t)r * kv_row_bytes + cc * 16;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void FA_LDS *)(dst + u * 1024), 16, goff, 0, 0, 0);
       }
     }
@@ -509,11 +562,27 @@ fa_fwd_kernel(FaArgs a) {
   const float c = a.scale_log2;
   const LdsAddr ad = lds_addr<D>(lane);
 
-  const int nkt = (nk + BC - 1) / BC;
-  const int nfull = nk / BC;  // tiles with no key past the end
+  // Masking per 32-row block nb: tiles below kfull[nb] hold no masked key for any row of the
+  // block; in the others, lane's row sees keys below klim[nb] (the sequence end, and under
+  // the causal mask its own index + 1).  Keys from wave_kend on are masked for every row of
+  // the wavefront.
+  int kfull[NB], klim[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int r0 = wrow0 + 32 * nb;
+    kfull[nb] = (a.causal ? min(nk, r0 + 1) : nk) / BC;
+    klim[nb] = a.causal ? min(nk, r0 + (lane & 31) + 1) : nk;
+  }
+  const int wave_kend = a.causal ? min(nk, wrow0 + QW) : nk;
   auto softmax = [&](f32x16 (&S)[KB], i32x4 (&P)[KS], int nb, int j, bool &rescale) __attribute__((always_inline)) {
-    if (j < nfull) return softmax_block<BC, F16, false>(S, P, m[nb], l[nb], c, 0, rescale);
-    return softmax_block<BC, F16, true>(S, P, m[nb], l[nb], c, nk - j * BC - 4 * hi, rescale);
+    if (j < kfull[nb]) return softmax_block<BC, F16, false>(S, P, m[nb], l[nb], c, 0, rescale);
+    return softmax_block<BC, F16, true>(S, P, m[nb], l[nb], c, klim[nb] - j * BC - 4 * hi, rescale);
+  };
+  auto finish = [&](int nb) __attribute__((always_inline)) {
+    if (nsplit > 1)
+      store_block_part<D>(O[nb], m[nb], l[nb], c, wrow0 + 32 * nb, nq, rp, lse_part_row, lane);
+    else
+      store_block<D, F16>(O[nb], m[nb], l[nb], c, wrow0 + 32 * nb, nq, row_bytes, ro, lse_row, lane);
   };
 
   if constexpr (SCHED == 0) {
@@ -528,13 +597,13 @@ fa_fwd_kernel(FaArgs a) {
       if constexpr (STAGES == 1) {
         if (j > 0) {
           __syncthreads();  // everyone is done with tile j-1
-          load_one(rk, smem, j);
-          load_one(rv, smem + TILE, j);
+          load_one(rk, smem, jb + j);
+          load_one(rv, smem + TILE, jb + j);
         }
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       } else {
         // this wavefront's pieces of tile j landed: at most the later tiles' loads pending
-        const int ahead = min(STAGES - 2, nkt - 1 - j);
+        const int ahead = min(STAGES - 2, ntl - 1 - j);
         if (ahead <= 0)
           wait_vmcnt<0>();
         else if (STAGES < 4 || ahead == 1)
@@ -545,32 +614,34 @@ fa_fwd_kernel(FaArgs a) {
       wg_barrier();  // ... and everyone's; and everyone is done with tile j - 1
       if constexpr (STAGES >= 2) {
         constexpr int NS = (ST + STAGES - 1) % STAGES;  // stage of tile j + STAGES - 1
-        if (j + STAGES - 1 < nkt) {
-          load_one(rk, smem + NS * STAGE, j + STAGES - 1);
-          load_one(rv, smem + NS * STAGE + TILE, j + STAGES - 1);
+        if (j + STAGES - 1 < ntl) {
+          load_one(rk, smem + NS * STAGE, jb + j + STAGES - 1);
+          load_one(rv, smem + NS * STAGE + TILE, jb + j + STAGES - 1);
         }
       }
-      f32x16 S[KB];
-      i32x4 P[KS];
-      bool rs;
-      qk_block<D, BC, F16>(smem + ST * STAGE, S, qreg[0], ad);
-      const float alpha = softmax(S, P, 0, j, rs);
-      if (rs) rescale_o<DT>(O[0], alpha);
-      pv_block<D, BC, F16>(smem + ST * STAGE + TILE, P, O[0], ad);
+      if ((jb + j) * BC < wave_kend) {  // else every key of the tile is masked for this wavefront
+        f32x16 S[KB];
+        i32x4 P[KS];
+        bool rs;
+        qk_block<D, BC, F16>(smem + ST * STAGE, S, qreg[0], ad);
+        const float alpha = softmax(S, P, 0, jb + j, rs);
+        if (rs) rescale_o<DT>(O[0], alpha);
+        pv_block<D, BC, F16>(smem + ST * STAGE + TILE, P, O[0], ad);
+      }
     };
 #pragma unroll
     for (int t = 0; t < (STAGES > 1 ? STAGES - 1 : 1); ++t) {
-      if (t < nkt) {
-        load_one(rk, smem + t * STAGE, t);
-        load_one(rv, smem + t * STAGE + TILE, t);
+      if (t < ntl) {
+        load_one(rk, smem + t * STAGE, jb + t);
+        load_one(rv, smem + t * STAGE + TILE, jb + t);
       }
     }
-    for (int j = 0; j < nkt; j += STAGES) {
+    for (int j = 0; j < ntl; j += STAGES) {
       static_for<0, STAGES>([&](auto st_c) __attribute__((always_inline)) {
-        if (j + decltype(st_c)::value < nkt) step(st_c, j + decltype(st_c)::value);
+        if (j + decltype(st_c)::value < ntl) step(st_c, j + decltype(st_c)::value);
       });
     }
-    store_block<D, F16>(O[0], m[0], l[0], c, wrow0, nq, row_bytes, ro, lse_row, lane);
+    finish(0);
   } else if constexpr (SCHED == 1) {
     // Dual-block software pipeline (see the header comment).  Step j:
     //   issue loads K(j+1) -> K slot (j+1)%2 (held K(j-1), last read in step j-1) and
@@ -586,35 +657,37 @@ fa_fwd_kernel(FaArgs a) {
     bool rs[2] = {false, false};
     auto kslot = [&](int j) __attribute__((always_inline)) { return smem + (j & 1) * TILE; };
     auto vslot = [&](int j) __attribute__((always_inline)) { return smem + 2 * TILE + (j % 3) * TILE; };
-    load_one(rk, kslot(0), 0);
-    load_one(rv, vslot(0), 0);
-    for (int j = 0; j <= nkt; ++j) {
+    if (ntl > 0) {
+      load_one(rk, kslot(0), jb);
+      load_one(rv, vslot(0), jb);
+    }
+    for (int j = 0; j <= ntl; ++j) {
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
-      if (j + 1 < nkt) {
-        load_one(rk, kslot(j + 1), j + 1);
-        load_one(rv, vslot(j + 1), j + 1);
+      if (j + 1 < ntl) {
+        load_one(rk, kslot(j + 1), jb + j + 1);
+        load_one(rv, vslot(j + 1), jb + j + 1);
       }
       // 1.
-      if (j < nkt) qk_block<D, BC, F16>(kslot(j), S[0], qreg[0], ad);
-      if (j >= 1) alpha[1] = softmax(S[1], P[1], 1, j - 1, rs[1]);
+      if (j < ntl) qk_block<D, BC, F16>(kslot(j), S[0], qreg[0], ad);
+      if (j >= 1) alpha[1] = softmax(S[1], P[1], 1, jb + j - 1, rs[1]);
       __builtin_amdgcn_sched_barrier(0);
       // 2.
       if (j >= 1) {
         if (rs[1]) rescale_o<DT>(O[1], alpha[1]);
         pv_block<D, BC, F16>(vslot(j - 1), P[1], O[1], ad);
       }
-      if (j < nkt) alpha[0] = softmax(S[0], P[0], 0, j, rs[0]);
+      if (j < ntl) alpha[0] = softmax(S[0], P[0], 0, jb + j, rs[0]);
       __builtin_amdgcn_sched_barrier(0);
       // 3. and 4.
-      if (j < nkt) {
+      if (j < ntl) {
         qk_block<D, BC, F16>(kslot(j), S[1], qreg[1], ad);
         if (rs[0]) rescale_o<DT>(O[0], alpha[0]);
         pv_block<D, BC, F16>(vslot(j), P[0], O[0], ad);
       }
     }
-    store_block<D, F16>(O[0], m[0], l[0], c, wrow0, nq, row_bytes, ro, lse_row, lane);
-    store_block<D, F16>(O[1], m[1], l[1], c, wrow0 + 32, nq, row_bytes, ro, lse_row, lane);
+    finish(0);
+    finish(1);
   } else {
     // Ping-pong over two groups of four wavefronts (see the header comment).  Every
     // wavefront runs the same program, step j = MMA(j) | barrier | SM(j) | barrier, where
@@ -632,28 +705,28 @@ fa_fwd_kernel(FaArgs a) {
     i32x4 P[KS];
     auto kslot = [&](int j) __attribute__((always_inline)) { return smem + (j & 1) * TILE; };
     auto vslot = [&](int j) __attribute__((always_inline)) { return smem + 2 * TILE + (j & 1) * TILE; };
-    load_one(rk, kslot(0), 0);
+    if (ntl > 0) load_one(rk, kslot(0), jb);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     wg_barrier();
     if (grp == 1) wg_barrier();
-    for (int j = 0; j <= nkt; ++j) {
+    for (int j = 0; j <= ntl; ++j) {
       if (grp == 0) {
-        if (j + 1 < nkt) load_by(rk, kslot(j + 1), j + 1, gw, Four{});
-        if (j < nkt) load_by(rv, vslot(j), j, gw, Four{});
+        if (j + 1 < ntl) load_by(rk, kslot(j + 1), jb + j + 1, gw, Four{});
+        if (j < ntl) load_by(rv, vslot(j), jb + j, gw, Four{});
       }
       if (j >= 1) pv_block<D, BC, F16>(vslot(j - 1), P, O[0], ad);
-      if (j < nkt) qk_block<D, BC, F16>(kslot(j), S, qreg[0], ad);
+      if (j < ntl) qk_block<D, BC, F16>(kslot(j), S, qreg[0], ad);
       wg_barrier();
-      if (j < nkt) {
+      if (j < ntl) {
         bool rs;
-        const float alpha = softmax(S, P, 0, j, rs);
+        const float alpha = softmax(S, P, 0, jb + j, rs);
         if (rs) rescale_o<DT>(O[0], alpha);
       }
       if (grp == 0) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       wg_barrier();
     }
     if (grp == 0) wg_barrier();
-    store_block<D, F16>(O[0], m[0], l[0], c, wrow0, nq, row_bytes, ro, lse_row, lane);
+    finish(0);
   }
 }
 

@@ -19,12 +19,33 @@ struct FaArgs {
   int seqlen_q;  // dense: Nq; varlen: max sequence length (also the LSE row pitch)
   int seqlen_k;  // dense: Nk; varlen: max sequence length
   int heads;
-  int n_qtiles;   // ceil(seqlen_q / br)
-  int total_wgs;  // batch * heads * n_qtiles
+  int heads_kv;  // K/V heads; query head h reads K/V head h / group
+  int group;     // heads / heads_kv
+  int causal;    // nonzero: key j is masked for query i when j > i
+  int num_splits;  // key tiles of each query tile are divided among this many workgroups
+  int n_qtiles;    // ceil(seqlen_q / br)
+  int total_wgs;   // batch * heads * n_qtiles * num_splits
   float scale_log2;  // scale * log2(e): scores go through exp2
+  // num_splits > 1: each workgroup writes its split's normalised fp32 output and natural-log
+  // LSE here instead of o / lse; the merge kernel combines them.
+  float *o_part;    // [num_splits, batch, heads, seqlen_q, D]
+  float *lse_part;  // [num_splits, batch, heads, seqlen_q]
+};
+
+// Arguments of the split merge kernel.
+struct MergeArgs {
+  const float *o_part;
+  const float *lse_part;
+  void *o;
+  float *lse;
+  const int32_t *cu_seqlens;
+  int batch, seqlen_q, heads, num_splits;
 };
 
 typedef hipError_t (*LaunchFn)(const FaArgs &, hipStream_t);
+
+// Launch the merge of num_splits partial results (defined in fa_merge.hip).
+hipError_t launch_merge(const MergeArgs &a, int d_head, int dtype, hipStream_t stream);
 
 // One compiled kernel configuration.
 struct KernelEntry {

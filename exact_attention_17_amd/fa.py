@@ -12,10 +12,11 @@ LIB_PATH = os.path.join(PKG, "libfa_fwd.so")
 
 FA_BF16, FA_FP16 = 0, 1
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_MISALIGNED, FA_ERR_HIP = 0, 1, 2, 3, 4
+FA_MAX_SPLITS = 128
 
 # Every exported symbol of include/fa_fwd.h.
-EXPORTS = ("fa_fwd", "fa_fwd_autotune", "fa_fwd_set_config", "fa_fwd_get_config",
-           "fa_fwd_num_configs", "fa_fwd_list_configs", "fa_fwd_config_lds_bytes",
+EXPORTS = ("fa_fwd", "fa_fwd_ext", "fa_fwd_workspace_bytes", "fa_fwd_choose_splits",
+           "fa_fwd_autotune", "fa_fwd_set_config", "fa_fwd_get_config", "fa_fwd_num_configs", "fa_fwd_list_configs", "fa_fwd_config_lds_bytes",
            "fa_fwd_config_resources", "fa_last_error", "fa_version")
 
 
@@ -54,6 +55,13 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         L.fa_fwd.restype = _i
         L.fa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.c_float, _vp, _i, _vp]
+        L.fa_fwd_ext.restype = _i
+        L.fa_fwd_ext.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, ctypes.c_float, _i, _vp, _i,
+                                 _i, _vp, ctypes.c_size_t, _vp]
+        L.fa_fwd_workspace_bytes.restype = ctypes.c_size_t
+        L.fa_fwd_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+        L.fa_fwd_choose_splits.restype = _i
+        L.fa_fwd_choose_splits.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
         L.fa_fwd_autotune.restype = _i
         L.fa_fwd_autotune.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.c_float, _vp,
                                       _i, _vp, _i, ctypes.POINTER(TileConfig),
@@ -116,19 +124,33 @@ def _stream_handle(stream, device):
     return stream.cuda_stream
 
 
-def _shape_args(q, k, v, cu_seqlens, max_seqlen):
+def _shape_args(q, k, v, cu_seqlens, max_seqlen, grouped=False):
+    """-> (batch, seqlen_q, seqlen_k, n_heads, n_heads_kv, d_head).  The library checks that
+    n_heads_kv divides n_heads; without grouped, k and v must have q's head count."""
     if cu_seqlens is None:
         if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
             raise ValueError("dense q, k, v must be [B, N, H, D] with k and v alike")
         batch, nq, heads, d = q.shape
-        if k.shape[0] != batch or k.shape[2] != heads or k.shape[3] != d:
+        if k.shape[0] != batch or k.shape[3] != d or (not grouped and k.shape[2] != heads):
             raise ValueError("q and k disagree on batch, heads or d_head")
-        return batch, nq, k.shape[1], heads, d
-    if q.dim() != 3 or q.shape != k.shape or k.shape != v.shape:
-        raise ValueError("varlen q, k, v must all be [total, H, D]")
+        return batch, nq, k.shape[1], heads, k.shape[2], d
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or k.shape[0] != q.shape[0] or \
+            k.shape[2] != q.shape[2] or (not grouped and k.shape[1] != q.shape[1]):
+        raise ValueError("varlen q must be [total, H, D] and k, v [total, H (or Hkv), D]")
     if max_seqlen is None:
         raise ValueError("varlen calls need max_seqlen")
-    return cu_seqlens.numel() - 1, int(max_seqlen), int(max_seqlen), q.shape[1], q.shape[2]
+    return cu_seqlens.numel() - 1, int(max_seqlen), int(max_seqlen), q.shape[1], k.shape[1], q.shape[2]
+
+
+def _check_tensors(q, k, v, cu_seqlens):
+    import torch
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
+        raise TypeError("cu_seqlens must be an int32 device tensor")
 
 
 def fa_fwd(q, k, v, o=None, lse=None, scale=None, cu_seqlens=None, max_seqlen=None, stream=None):
@@ -140,14 +162,8 @@ def fa_fwd(q, k, v, o=None, lse=None, scale=None, cu_seqlens=None, max_seqlen=No
     o and lse may be given (preallocated); otherwise they are allocated with torch.
     """
     import torch
-    batch, nq, nk, heads, d = _shape_args(q, k, v, cu_seqlens, max_seqlen)
-    for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous device tensors")
-    if q.dtype != k.dtype or q.dtype != v.dtype:
-        raise TypeError("q, k, v must share one dtype")
-    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
-        raise TypeError("cu_seqlens must be an int32 device tensor")
+    batch, nq, nk, heads, _, d = _shape_args(q, k, v, cu_seqlens, max_seqlen)
+    _check_tensors(q, k, v, cu_seqlens)
     if scale is None:
         scale = d ** -0.5
     if o is None:
@@ -161,9 +177,64 @@ def fa_fwd(q, k, v, o=None, lse=None, scale=None, cu_seqlens=None, max_seqlen=No
     return o, lse
 
 
+def fa_fwd_ext(q, k, v, o=None, lse=None, scale=None, causal=False, cu_seqlens=None, max_seqlen=None,
+               num_splits=1, workspace=None, stream=None):
+    """Attention forward with grouped K/V heads, the causal mask and split keys; returns (o, lse).
+
+    k and v may have fewer heads than q (a divisor of them: MQA/GQA).  causal masks key j for
+    query i when j > i.  num_splits: 1 = no split, 0 = automatic, n > 1 = n splits.  A split
+    call needs a device workspace of fa_fwd_workspace_bytes(...) bytes; when workspace is None
+    one is allocated with torch (for num_splits = 0, sized for the automatic count).
+    """
+    import torch
+    batch, nq, nk, heads, heads_kv, d = _shape_args(q, k, v, cu_seqlens, max_seqlen, grouped=True)
+    _check_tensors(q, k, v, cu_seqlens)
+    if scale is None:
+        scale = d ** -0.5
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((batch, heads, nq), dtype=torch.float32, device=q.device)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if not workspace.is_cuda:
+            raise ValueError("workspace must be a device tensor")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    elif num_splits != 1:
+        n = num_splits if num_splits > 1 else fa_fwd_choose_splits(
+            batch, nq, nk, heads, d, _dtype_code(q), causal, cu_seqlens is not None)
+        if n > 1:
+            workspace = torch.empty(fa_fwd_workspace_bytes(batch, nq, heads, d, n), dtype=torch.uint8,
+                                    device=q.device)
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    st = lib().fa_fwd_ext(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), batch, nq,
+                          nk, heads, heads_kv, d, float(scale), int(bool(causal)),
+                          cu_seqlens.data_ptr() if cu_seqlens is not None else None, _dtype_code(q),
+                          int(num_splits), ws_ptr, ws_bytes, _stream_handle(stream, q.device))
+    _check(st)
+    return o, lse
+
+
+def fa_fwd_workspace_bytes(batch, seqlen_q, n_heads, d_head, num_splits):
+    """Workspace bytes fa_fwd_ext needs for num_splits splits (0 for one)."""
+    n = lib().fa_fwd_workspace_bytes(batch, seqlen_q, n_heads, d_head, num_splits)
+    if n == 0 and num_splits != 1:
+        raise FaError(FA_ERR_INVALID_ARG, fa_last_error())
+    return n
+
+
+def fa_fwd_choose_splits(batch, seqlen_q, seqlen_k, n_heads, d_head, dtype, causal=False, varlen=False):
+    """The split count fa_fwd_ext's automatic choice starts from."""
+    n = lib().fa_fwd_choose_splits(batch, seqlen_q, seqlen_k, n_heads, d_head, dtype, int(bool(causal)),
+                                   int(bool(varlen)))
+    if n < 0:
+        raise FaError(-n, fa_last_error())
+    return n
+
+
 def fa_fwd_autotune(q, k, v, o, lse, scale=None, cu_seqlens=None, max_seqlen=None, reps=5, stream=None):
     """Time every admissible compiled configuration on these buffers; returns (TileConfig, ms)."""
-    batch, nq, nk, heads, d = _shape_args(q, k, v, cu_seqlens, max_seqlen)
+    batch, nq, nk, heads, _, d = _shape_args(q, k, v, cu_seqlens, max_seqlen)
     if scale is None:
         scale = d ** -0.5
     chosen = TileConfig()

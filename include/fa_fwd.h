@@ -16,8 +16,8 @@
  *
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The
- *    library allocates no device memory in fa_fwd and keeps no pointer after
- *    a call returns.
+ *    library allocates no device memory in fa_fwd or fa_fwd_ext and keeps no
+ *    pointer after a call returns.
  *  - Dense layout (cu_seqlens == NULL):
  *      q, o : [batch, seqlen_q, n_heads, d_head], contiguous
  *      k, v : [batch, seqlen_k, n_heads, d_head], contiguous
@@ -43,6 +43,7 @@
 #ifndef FA_FWD_H
 #define FA_FWD_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -92,6 +93,60 @@ typedef struct {
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
            int seqlen_q, int seqlen_k, int n_heads, int d_head, float scale,
            const int32_t *cu_seqlens, int dtype, void *stream);
+
+/* Largest num_splits fa_fwd_ext accepts. */
+#define FA_MAX_SPLITS 128
+
+/* The forward pass with the options of page "GPU 内核与 FlashAttention",
+ * section 14:
+ *  - n_heads_kv: K/V heads (MQA/GQA, section 14.2).  It must divide n_heads;
+ *    query head h reads K/V head h / (n_heads / n_heads_kv), and nothing is
+ *    copied.  k and v are then [batch, seqlen_k, n_heads_kv, d_head] (packed:
+ *    [cu[batch], n_heads_kv, d_head]); q, o and lse are as in fa_fwd.
+ *    n_heads_kv == n_heads is ordinary multi-head attention.
+ *  - causal (0 or 1; section 14.4): the score of key j for query i is -inf
+ *    when j > i, with i and j counted from the start of the sequence (so
+ *    for seqlen_q != seqlen_k query i sees keys 0..i: top-left aligned).
+ *    Key tiles lying wholly above the diagonal are never loaded or computed;
+ *    only tiles crossing it are masked element by element.
+ *  - num_splits: the keys each query tile visits are divided among this many
+ *    workgroups, whose partial results are merged with the (m, l) merge of
+ *    section 11.2 by a second kernel on the same stream.  This fills the GPU
+ *    when batch x heads x query tiles is small next to the 256 CUs and the
+ *    key range is long (a few query rows over many keys).
+ *      1            : no split; workspace may be NULL.
+ *      2 .. FA_MAX_SPLITS : that many splits; workspace must hold at least
+ *                     fa_fwd_workspace_bytes(batch, seqlen_q, n_heads,
+ *                     d_head, num_splits) bytes, 16-byte aligned.
+ *      0            : automatic: fa_fwd_choose_splits(...), lowered to the
+ *                     largest count whose workspace fits workspace_bytes
+ *                     (1 if workspace is NULL).
+ *    workspace is device memory owned by the caller, used only while the
+ *    call's work runs on `stream`; its contents before and after are
+ *    irrelevant.  Calls sharing one workspace must be ordered on a stream.
+ *    The result equals the unsplit one up to fp32 rounding order.
+ * fa_fwd(q, k, v, o, lse, b, nq, nk, h, d, scale, cu, dtype, stream) is
+ * fa_fwd_ext(q, k, v, o, lse, b, nq, nk, h, h, d, scale, 0, cu, dtype, 1,
+ * NULL, 0, stream).  Returns an fa_status_t. */
+int fa_fwd_ext(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
+               int seqlen_q, int seqlen_k, int n_heads, int n_heads_kv, int d_head, float scale,
+               int causal, const int32_t *cu_seqlens, int dtype, int num_splits, void *workspace,
+               size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace fa_fwd_ext needs for num_splits splits:
+ * num_splits x batch x n_heads x seqlen_q x (d_head + 1) x 4 (each split's
+ * fp32 output rows and natural-log LSE; packed layout: seqlen_q is the
+ * longest length).  0 for num_splits == 1, and 0 with fa_last_error() set
+ * on bad arguments.  Host-only. */
+size_t fa_fwd_workspace_bytes(int batch, int seqlen_q, int n_heads, int d_head, int num_splits);
+
+/* The split count num_splits = 0 resolves to before the workspace limit:
+ * 1 when batch x n_heads x query tiles already gives every CU work, else
+ * enough splits for about two workgroups per CU, at most one per two key
+ * tiles and at most FA_MAX_SPLITS.  causal and varlen are 0 or 1.
+ * Host-only; < 0 on bad arguments. */
+int fa_fwd_choose_splits(int batch, int seqlen_q, int seqlen_k, int n_heads, int d_head, int dtype,
+                         int causal, int varlen);
 
 /* Tile autotuner (page "Flash Attention 2 Chapter6", Kernel 7: enumerate the
  * configuration space, drop configurations that spill registers or do not

@@ -136,3 +136,73 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 8, 1, 32, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.fa_fwd(q, q, q)
+
+
+def call_ext(**over):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, batch=1, seqlen_q=128, seqlen_k=128, n_heads=4, n_heads_kv=2,
+                d_head=64, scale=0.125, causal=1, cu_seqlens=None, dtype=fa.FA_BF16, num_splits=4,
+                workspace=A, workspace_bytes=1 << 30, stream=None)
+    args.update(over)
+    L = fa.lib()
+    return L.fa_fwd_ext(args["q"], args["k"], args["v"], args["o"], args["lse"], args["batch"],
+                        args["seqlen_q"], args["seqlen_k"], args["n_heads"], args["n_heads_kv"],
+                        args["d_head"], ctypes.c_float(args["scale"]), args["causal"], args["cu_seqlens"],
+                        args["dtype"], args["num_splits"], args["workspace"], args["workspace_bytes"],
+                        args["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(n_heads_kv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(n_heads_kv=3), fa.FA_ERR_INVALID_ARG),          # does not divide 4
+    (dict(n_heads_kv=8), fa.FA_ERR_INVALID_ARG),          # more K/V heads than query heads
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(num_splits=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(num_splits=fa.FA_MAX_SPLITS + 1), fa.FA_ERR_INVALID_ARG),
+    (dict(workspace=None), fa.FA_ERR_INVALID_ARG),        # 4 splits need a workspace
+    (dict(workspace=A + 8), fa.FA_ERR_MISALIGNED),
+    (dict(workspace_bytes=4 * 128 * 4 * 65 * 4 - 1), fa.FA_ERR_INVALID_ARG),  # one byte short
+    (dict(d_head=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(cu_seqlens=A, seqlen_q=64, seqlen_k=128), fa.FA_ERR_INVALID_ARG),
+])
+def test_ext_bad_arguments_rejected_on_host(over, status):
+    assert call_ext(**over) == status
+    assert fa.fa_last_error() != ""
+
+
+def test_workspace_bytes():
+    # splits x batch x heads x seqlen_q x (d + 1) x 4
+    assert fa.fa_fwd_workspace_bytes(1, 128, 4, 64, 4) == 4 * 128 * 4 * 65 * 4
+    assert fa.fa_fwd_workspace_bytes(2, 64, 1, 128, 32) == 32 * 2 * 64 * 129 * 4
+    assert fa.fa_fwd_workspace_bytes(3, 10, 2, 32, 1) == 0
+    for bad in ((0, 128, 4, 64, 4), (1, 128, 4, 64, 0), (1, 128, 4, 64, fa.FA_MAX_SPLITS + 1)):
+        with pytest.raises(fa.FaError):
+            fa.fa_fwd_workspace_bytes(*bad)
+    with pytest.raises(fa.FaError):
+        fa.fa_fwd_workspace_bytes(1, 128, 4, 48, 4)
+
+
+def test_choose_splits():
+    # 64 queries over 4096 keys, one head: one workgroup alone -> split, at most one split per
+    # two 64-key tiles
+    assert fa.fa_fwd_choose_splits(1, 64, 4096, 1, 128, fa.FA_BF16) == 32
+    # a grid that already covers the CUs is not split
+    assert fa.fa_fwd_choose_splits(16, 4096, 4096, 16, 128, fa.FA_BF16) == 1
+    # few keys: no split possible
+    assert fa.fa_fwd_choose_splits(1, 64, 64, 1, 64, fa.FA_BF16) == 1
+    # causal top-left: 64 queries see at most 64 keys
+    assert fa.fa_fwd_choose_splits(1, 64, 4096, 1, 128, fa.FA_BF16, causal=True) == 1
+    n = fa.fa_fwd_choose_splits(2, 256, 8192, 4, 128, fa.FA_BF16)
+    assert 1 < n <= fa.FA_MAX_SPLITS
+    with pytest.raises(fa.FaError):
+        fa.fa_fwd_choose_splits(0, 64, 4096, 1, 128, fa.FA_BF16)
+
+
+def test_ext_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 8, 4, 32, dtype=torch.bfloat16)
+    k = torch.zeros(1, 8, 2, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa_fwd_ext(q, k, k, causal=True)

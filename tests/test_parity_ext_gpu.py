@@ -1,0 +1,226 @@
+"""GPU parity of the extended forward (fa_fwd_ext): the causal mask with tile skipping,
+grouped K/V heads (MQA/GQA) and the split key range with its merge kernel, against the
+fp64 oracle on the same seeded inputs.
+
+Bar as for the plain forward: O max-abs error <= 2e-2 and mean-abs <= 2e-3, LSE max-abs
+<= 1e-3.  Small shapes are compared in full, the full-size workloads on sampled rows.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_17_amd import fa, inputs
+
+pytestmark = pytest.mark.gpu
+
+O_MAX, O_MEAN, LSE_MAX = 2e-2, 2e-3, 1e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_ext(q, k, v, scale, causal=False, num_splits=1, cu=None, max_seqlen=None, lse_fill=None,
+            workspace=None):
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    cud = cu.to(dev) if cu is not None else None
+    lse = None
+    if lse_fill is not None:
+        batch = cu.numel() - 1 if cu is not None else q.shape[0]
+        nq = max_seqlen if cu is not None else q.shape[1]
+        lse = torch.full((batch, q.shape[-2], nq), lse_fill, dtype=torch.float32, device=dev)
+    o, lse = fa.fa_fwd_ext(qd, kd, vd, lse=lse, scale=scale, causal=causal, cu_seqlens=cud,
+                           max_seqlen=max_seqlen, num_splits=num_splits, workspace=workspace)
+    torch.cuda.synchronize()
+    return o.cpu().to(torch.float64).numpy(), lse.cpu().to(torch.float64).numpy()
+
+
+def assert_close(o_gpu, o_ref, lse_gpu, lse_ref, what):
+    err = np.abs(o_gpu - o_ref)
+    lerr = np.abs(lse_gpu - lse_ref)
+    say("%s: O max %.3g mean %.3g  LSE max %.3g" % (what, err.max(), err.mean(), lerr.max()))
+    assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(lse_gpu)), what
+    assert err.max() <= O_MAX, what
+    assert err.mean() <= O_MEAN, what
+    assert lerr.max() <= LSE_MAX, what
+
+
+def check_dense(q, k, v, scale, what, causal=False, num_splits=1):
+    say("case %s q%s k%s causal=%d splits=%d" % (what, tuple(q.shape), tuple(k.shape), causal, num_splits))
+    o_g, lse_g = run_ext(q, k, v, scale, causal=causal, num_splits=num_splits)
+    o_r, lse_r = oracle.attention(inputs.to_f64(q), inputs.to_f64(k), inputs.to_f64(v), scale, causal=causal)
+    assert_close(o_g, o_r, lse_g, lse_r, what)
+    return o_g, lse_g
+
+
+def check_varlen(lengths, heads, heads_kv, d, dtype, seed, what, causal=False, num_splits=1):
+    q, k, v, cu, max_len = inputs.varlen_qkv(heads=heads, d_head=d, dtype=dtype, seed=seed, lengths=lengths,
+                                             heads_kv=heads_kv)
+    say("case %s lengths %s H%d Hkv%d causal=%d splits=%d" % (what, lengths, heads, heads_kv, causal, num_splits))
+    scale = d ** -0.5
+    o_g, lse_g = run_ext(q, k, v, scale, causal=causal, num_splits=num_splits, cu=cu, max_seqlen=max_len,
+                         lse_fill=float("nan"))
+    o_r, lse_r = oracle.attention(inputs.to_f64(q), inputs.to_f64(k), inputs.to_f64(v), scale,
+                                  cu_seqlens=cu.numpy(), max_seqlen=max_len, causal=causal)
+    valid = np.zeros(lse_g.shape, dtype=bool)
+    for b, L in enumerate(lengths):
+        valid[b, :, :L] = True
+    assert np.all(np.isnan(lse_g[~valid])), "LSE padding rows were written"
+    assert_close(o_g, o_r, lse_g[valid], lse_r[valid], what)
+
+
+# ------------------------------------------------------------------------------------ causal
+@pytest.mark.parametrize("nq,nk,d,dtype", [
+    (128, 128, 64, "bf16"), (1, 1, 32, "bf16"), (63, 63, 64, "fp16"), (200, 200, 128, "bf16"),
+    (513, 513, 128, "bf16"), (300, 100, 64, "bf16"), (100, 300, 128, "fp16"), (1000, 1000, 32, "fp16"),
+    (1100, 1100, 128, "bf16"), (257, 257, 32, "bf16"),
+])
+def test_causal_ragged(nq, nk, d, dtype):
+    q, k, v = inputs.dense_qkv(2, nq, nk, 2, d, dtype, seed=nq * 11 + nk)
+    check_dense(q, k, v, d ** -0.5, "causal nq%d nk%d d%d %s" % (nq, nk, d, dtype), causal=True)
+
+
+@pytest.mark.parametrize("d,dtype", [(32, "bf16"), (64, "fp16"), (128, "bf16"), (128, "fp16")])
+def test_causal_every_config(d, dtype):
+    """Each compiled tile configuration, schedules 1 and 2 included, under the causal mask."""
+    code = fa.FA_BF16 if dtype == "bf16" else fa.FA_FP16
+    q, k, v = inputs.dense_qkv(1, 300, 300, 2, d, dtype, seed=d + code)
+    o_r, lse_r = oracle.attention(inputs.to_f64(q), inputs.to_f64(k), inputs.to_f64(v), d ** -0.5, causal=True)
+    try:
+        for c in fa.fa_fwd_list_configs(d, code):
+            if fa.fa_fwd_config_lds_bytes(d, c) > 160 * 1024:
+                continue
+            fa.fa_fwd_set_config(d, code, c)
+            say("case causal config %s d%d %s" % (c.as_tuple(), d, dtype))
+            o_g, lse_g = run_ext(q, k, v, d ** -0.5, causal=True)
+            assert_close(o_g, o_r, lse_g, lse_r, "causal %s d%d %s" % (c.as_tuple(), d, dtype))
+    finally:
+        fa.fa_fwd_set_config(d, code, None)
+
+
+def test_causal_repeat_bitwise():
+    q, k, v = inputs.dense_qkv(2, 700, 700, 4, 128, "bf16", seed=77)
+    a = run_ext(q, k, v, 128 ** -0.5, causal=True)
+    b = run_ext(q, k, v, 128 ** -0.5, causal=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_causal_first_row_is_first_value():
+    """Query 0 sees only key 0: O row 0 is v_0 rounded, LSE row 0 is its own score."""
+    q, k, v = inputs.dense_qkv(1, 260, 260, 2, 64, "bf16", seed=5)
+    o_g, lse_g = run_ext(q, k, v, 0.125, causal=True)
+    v0 = inputs.to_f64(v)[0, 0]
+    assert np.array_equal(o_g[0, 0], v0)
+    s00 = 0.125 * np.einsum("hd,hd->h", inputs.to_f64(q)[0, 0], inputs.to_f64(k)[0, 0])
+    assert np.max(np.abs(lse_g[0, :, 0] - s00)) <= 1e-5
+
+
+# ------------------------------------------------------------------------------ grouped heads
+@pytest.mark.parametrize("hkv", [1, 2, 4])
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_heads_dense(hkv, causal):
+    q, k, v = inputs.dense_qkv(2, 257, 257, 8, 128, "bf16", seed=30 + hkv, heads_kv=hkv)
+    check_dense(q, k, v, 128 ** -0.5, "gqa H8 Hkv%d" % hkv, causal=causal)
+
+
+@pytest.mark.parametrize("d,dtype", [(32, "fp16"), (64, "bf16")])
+def test_grouped_heads_small_d(d, dtype):
+    q, k, v = inputs.dense_qkv(3, 130, 190, 6, d, dtype, seed=d, heads_kv=3)
+    check_dense(q, k, v, d ** -0.5, "gqa H6 Hkv3 d%d" % d)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_heads_varlen(causal):
+    check_varlen([1, 130, 0, 64, 300], 8, 2, 128, "bf16", 41, "gqa varlen", causal=causal)
+
+
+# ------------------------------------------------------------------------------ split keys
+@pytest.mark.parametrize("splits", [2, 3, 7, 32, 64, 128])
+def test_split_slice_shape(splits):
+    """64 queries over 4096 keys; 128 splits leave 64 of them with no tile at all."""
+    w = inputs.workload("slice")
+    check_dense(w["q"], w["k"], w["v"], w["scale"], "slice split%d" % splits, num_splits=splits)
+
+
+@pytest.mark.parametrize("splits", [2, 5, 16])
+def test_split_causal(splits):
+    """Causal and split: later splits hold no visible key for the first rows of a tile."""
+    q, k, v = inputs.dense_qkv(1, 700, 700, 2, 128, "bf16", seed=splits)
+    check_dense(q, k, v, 128 ** -0.5, "causal split%d" % splits, causal=True, num_splits=splits)
+
+
+@pytest.mark.parametrize("d,dtype", [(32, "fp16"), (64, "bf16")])
+def test_split_small_d(d, dtype):
+    q, k, v = inputs.dense_qkv(2, 70, 1500, 3, d, dtype, seed=d + 1)
+    check_dense(q, k, v, d ** -0.5, "split6 d%d" % d, num_splits=6)
+
+
+def test_split_varlen_grouped_causal():
+    check_varlen([700, 1, 64, 0, 2000], 4, 2, 128, "bf16", 43, "varlen gqa causal split4", causal=True,
+                 num_splits=4)
+    check_varlen([700, 1, 64, 0, 2000], 4, 4, 64, "fp16", 44, "varlen split9", num_splits=9)
+
+
+def test_split_automatic_and_workspace_reuse():
+    """num_splits = 0 picks the automatic count; one workspace serves successive calls."""
+    w = inputs.workload("slice")
+    n = fa.fa_fwd_choose_splits(1, 64, 4096, 1, 128, fa.FA_BF16)
+    assert n > 1
+    ws = torch.empty(fa.fa_fwd_workspace_bytes(1, 64, 1, 128, n), dtype=torch.uint8, device="cuda:0")
+    o_r, lse_r = oracle.attention(inputs.to_f64(w["q"]), inputs.to_f64(w["k"]), inputs.to_f64(w["v"]), w["scale"])
+    for _ in range(2):
+        o_g, lse_g = run_ext(w["q"], w["k"], w["v"], w["scale"], num_splits=0, workspace=ws)
+        assert_close(o_g, o_r, lse_g, lse_r, "slice auto split %d" % n)
+    # a workspace too small for the automatic count lowers it instead of failing
+    small = torch.empty(fa.fa_fwd_workspace_bytes(1, 64, 1, 128, 3), dtype=torch.uint8, device="cuda:0")
+    o_g, lse_g = run_ext(w["q"], w["k"], w["v"], w["scale"], num_splits=0, workspace=small)
+    assert_close(o_g, o_r, lse_g, lse_r, "slice auto split within 3-split workspace")
+
+
+# --------------------------------------------------------------------------- full size
+def sample_rows(rng, batch, heads, length, n):
+    rows = [(int(rng.integers(batch)), int(rng.integers(heads)), int(rng.integers(length))) for _ in range(n)]
+    return rows + [(0, 0, 0), (0, 0, 1), (batch - 1, heads - 1, length - 1)]
+
+
+def compare_rows(o_g, lse_g, w, rows, what):
+    by_b = {}
+    for r in rows:
+        by_b.setdefault(r[0], []).append(r)
+    errs, lerrs = [], []
+    for b, rs in by_b.items():
+        o_r, lse_r = oracle.attention_rows(inputs.to_f64(w["q"][b:b + 1]), inputs.to_f64(w["k"][b:b + 1]),
+                                           inputs.to_f64(w["v"][b:b + 1]), w["scale"],
+                                           [(0, h, i) for (_, h, i) in rs], causal=w["causal"])
+        for n, (_, h, i) in enumerate(rs):
+            errs.append(np.abs(o_g[b, i, h] - o_r[n]))
+            lerrs.append(abs(lse_g[b, h, i] - lse_r[n]))
+    err = np.concatenate(errs)
+    say("%s (%d sampled rows): O max %.3g mean %.3g  LSE max %.3g" % (what, len(rows), err.max(), err.mean(),
+                                                                      max(lerrs)))
+    assert err.max() <= O_MAX and err.mean() <= O_MEAN and max(lerrs) <= LSE_MAX, what
+
+
+@pytest.mark.parametrize("name", ["causal", "gqa"])
+def test_full_size_workloads_sampled_rows(name):
+    w = inputs.workload(name)
+    say("case %s B%d N%d H%d Hkv%d d%d causal=%d" % (name, w["batch"], w["seqlen_q"], w["heads"], w["heads_kv"],
+                                                     w["d_head"], w["causal"]))
+    o_g, lse_g = run_ext(w["q"], w["k"], w["v"], w["scale"], causal=w["causal"])
+    assert np.all(np.isfinite(o_g)) and np.all(np.isfinite(lse_g))
+    rows = sample_rows(np.random.default_rng(len(name)), w["batch"], w["heads"], w["seqlen_q"], 160)
+    compare_rows(o_g, lse_g, w, rows, name)
