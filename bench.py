@@ -8,8 +8,11 @@ timing).  Prints ONE JSON line with the throughput in TFLOP/s
 (4 * B * H * Nq * Nk * d per step), the roofline figures of the kernel and the
 fp64 oracle timed on a bounded sample on the host cores.
 
-Other modes (used to produce the committed profiles):
-    --workload NAME     time another named workload (tiny, slice, full, small_head, varlen)
+Other modes (used to produce the committed profiles and the secondary measurements):
+    --workload NAME     time another named workload (tiny, slice, full, small_head, varlen,
+                        causal, gqa); causal counts only the visible (query, key) pairs
+    --splits N          key-range splits per query tile (fa_fwd_ext num_splits): 0 = the
+                        library's automatic choice (default), 1 = no split
     --copy-bytes N      run only a plain device copy of N bytes (the counter calibration)
     --no-cpu-baseline   skip the oracle timing
 """
@@ -26,6 +29,16 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA: 256 CU x 4 SIMD x 1024 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+HEADLINE_METRIC = "fwd TFLOP/s (4BHN\u00b2d) at B16\u00b7N4096\u00b7H16\u00b7d128 bf16; % of MFMA bf16 peak"
+WORKLOAD_NAMES = {
+    "full": "full B16 N4096 H16 d128 bf16 non-causal",
+    "tiny": "tiny B1 N128 H2 d64 bf16",
+    "slice": "slice B1 Nq64 Nk4096 H1 d128 bf16",
+    "small_head": "small_head B64 N512 H16 d32 fp16",
+    "varlen": "varlen 8 seqs U[512,8192] H16 d128 bf16",
+    "causal": "causal B16 N4096 H16 d128 bf16 (top-left causal mask)",
+    "gqa": "gqa B16 N4096 H16 Hkv2 d128 bf16 non-causal",
+}
 
 
 def log(msg):
@@ -33,10 +46,13 @@ def log(msg):
 
 
 def kernel_source_hash():
-    """Hash of the kernel sources; counter-derived traffic is only reported for the same kernel."""
+    """Hash of the forward kernel's device sources (the kernel template, the shared argument
+    header and the instantiation units); counter-derived traffic is only reported for the
+    same kernel."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "exact_attention_17_amd", "csrc", "*"))):
-        if p.endswith((".h", ".hip", ".cpp")):
+        base = os.path.basename(p)
+        if base == "fa_internal.h" or (base.startswith("fa_fwd_") and base.endswith((".h", ".hip"))):
             with open(p, "rb") as f:
                 h.update(os.path.basename(p).encode())
                 h.update(f.read())
@@ -84,27 +100,39 @@ def cpu_baseline(w, target_s=12.0):
 
     import oracle
     from exact_attention_17_amd import inputs
-    q = inputs.to_f64(w["q"][0:1])
-    k = inputs.to_f64(w["k"][0:1])
-    v = inputs.to_f64(w["v"][0:1])
-    nq, nk, heads, d = w["seqlen_q"], w["seqlen_k"], w["heads"], w["d_head"]
+    if w["cu_seqlens"] is not None:
+        s0, s1 = int(w["cu_seqlens"][0]), int(w["cu_seqlens"][1])
+        q, k, v = (inputs.to_f64(t[None, s0:s1]) for t in (w["q"], w["k"], w["v"]))
+        nq = nk = s1 - s0
+    else:
+        q, k, v = (inputs.to_f64(t[0:1]) for t in (w["q"], w["k"], w["v"]))
+        nq, nk = w["seqlen_q"], w["seqlen_k"]
+    heads, d, causal = w["heads"], w["d_head"], w["causal"]
     rng = np.random.default_rng(0)
+    picked = []
 
     def rows(n):
-        return [(0, int(rng.integers(heads)), int(rng.integers(nq))) for _ in range(n)]
+        r = [(0, int(rng.integers(heads)), int(rng.integers(nq))) for _ in range(n)]
+        picked[:] = r
+        return r
 
-    oracle.attention_rows(q, k, v, w["scale"], rows(8))  # warm (threads, pages)
+    def run(n):
+        oracle.attention_rows(q, k, v, w["scale"], rows(n), causal=causal)
+
+    run(8)  # warm (threads, pages)
     n = 64
     t0 = time.perf_counter()
-    oracle.attention_rows(q, k, v, w["scale"], rows(n))
+    run(n)
     t = time.perf_counter() - t0
     n = int(min(max(n * target_s / max(t, 1e-6), 64), 200000))
     t0 = time.perf_counter()
-    oracle.attention_rows(q, k, v, w["scale"], rows(n))
+    run(n)
     t = time.perf_counter() - t0
-    flops = 4.0 * n * nk * d
+    # work of the sampled rows: each row against its visible keys
+    flops = 4.0 * d * sum((min(i + 1, nk) if causal else nk) for (_, _, i) in picked)
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d random query rows of batch entry 0 (all %d keys, d %d), fp64, %.1f s" % (n, nk, d, t)}
+            "sample": "%d random query rows of batch entry 0 (%s %d keys, d %d), fp64, %.1f s"
+                      % (n, "visible ones of" if causal else "all", nk, d, t)}
 
 
 def main():
@@ -113,6 +141,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="full")
+    ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -142,20 +171,28 @@ def main():
     cu = w["cu_seqlens"].to(dev) if w["cu_seqlens"] is not None else None
     o = torch.empty_like(qd)
     lse = torch.empty((w["batch"], w["heads"], w["seqlen_q"]), dtype=torch.float32, device=dev)
+    causal, hkv = w["causal"], w["heads_kv"]
     if cu is None:
-        flops = metrics.fwd_flops(w["batch"], w["heads"], w["seqlen_q"], w["seqlen_k"], w["d_head"])
-        nbytes = metrics.fwd_bytes(w["batch"], w["heads"], w["seqlen_q"], w["seqlen_k"], w["d_head"])
+        flops = metrics.fwd_flops(w["batch"], w["heads"], w["seqlen_q"], w["seqlen_k"], w["d_head"], causal)
+        nbytes = metrics.fwd_bytes(w["batch"], w["heads"], w["seqlen_q"], w["seqlen_k"], w["d_head"],
+                                   heads_kv=hkv)
     else:
-        flops = metrics.varlen_fwd_flops(w["lengths"], w["heads"], w["d_head"])
-        nbytes = metrics.varlen_fwd_bytes(w["lengths"], w["heads"], w["d_head"])
+        flops = metrics.varlen_fwd_flops(w["lengths"], w["heads"], w["d_head"], causal)
+        nbytes = metrics.varlen_fwd_bytes(w["lengths"], w["heads"], w["d_head"], heads_kv=hkv)
     dtype_code = fa.FA_FP16 if w["dtype"] == "fp16" else fa.FA_BF16
     cfg = fa.fa_fwd_get_config(w["batch"], w["seqlen_q"], w["seqlen_k"], w["heads"], w["d_head"], dtype_code,
                                varlen=cu is not None)
+    splits = args.splits if args.splits > 0 else fa.fa_fwd_choose_splits(
+        w["batch"], w["seqlen_q"], w["seqlen_k"], w["heads"], w["d_head"], dtype_code, causal, cu is not None)
+    workspace = None
+    if splits > 1:  # allocated before timing; the library allocates nothing
+        workspace = torch.empty(fa.fa_fwd_workspace_bytes(w["batch"], w["seqlen_q"], w["heads"], w["d_head"],
+                                                          splits), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        fa.fa_fwd(qd, kd, vd, o, lse, scale=w["scale"], cu_seqlens=cu, max_seqlen=w["max_seqlen"],
-                  stream=stream)
+        fa.fa_fwd_ext(qd, kd, vd, o, lse, scale=w["scale"], causal=causal, cu_seqlens=cu,
+                      max_seqlen=w["max_seqlen"], num_splits=splits, workspace=workspace, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -171,9 +208,9 @@ def main():
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / args.steps
     tflops = flops / (ms * 1e-3) / 1e12
-    log("%s: %.4f ms per launch (wall %.4f ms), %.1f TFLOP/s, %.1f%% of %.1f, tiles %r"
+    log("%s: %.4f ms per step (wall %.4f ms), %.1f TFLOP/s, %.1f%% of %.1f, tiles %r, splits %d"
         % (args.workload, ms, wall * 1e3 / args.steps, tflops, 100 * tflops / PEAK_BF16_TFLOPS,
-           PEAK_BF16_TFLOPS, cfg))
+           PEAK_BF16_TFLOPS, cfg, splits))
 
     traffic = read_traffic(args.workload)
     cpu = None
@@ -182,11 +219,11 @@ def main():
         cpu = cpu_baseline(w)
         log("oracle: %.3g TFLOP/s on %d threads (%s)" % (cpu["value"], cpu["cores"], cpu["sample"]))
 
-    wl = {"full": "full B16 N4096 H16 d128 bf16 non-causal", "tiny": "tiny B1 N128 H2 d64 bf16",
-          "slice": "slice B1 Nq64 Nk4096 H1 d128 bf16", "small_head": "small_head B64 N512 H16 d32 fp16",
-          "varlen": "varlen 8 seqs U[512,8192] H16 d128 bf16"}[args.workload]
+    wl = WORKLOAD_NAMES[args.workload]
+    metric = HEADLINE_METRIC if args.workload == "full" else \
+        "fwd TFLOP/s (4 d x visible query-key pairs per batch and head) on %s; %% of MFMA bf16 peak" % wl
     out = {
-        "metric": "fwd TFLOP/s (4BHN^2d) at B16 N4096 H16 d128 bf16; % of MFMA bf16 peak",
+        "metric": metric,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -199,9 +236,10 @@ def main():
         "dtype": w["dtype"],
         "data": "synthetic (seeded N(0,1), rounded to %s)" % w["dtype"],
         "config": {"workload": wl, "batch": w["batch"], "seq_len_q": w["seqlen_q"], "seq_len_k": w["seqlen_k"],
-                   "heads": w["heads"], "d_head": w["d_head"], "causal": False,
-                   "tile": {"br": cfg.br, "bc": cfg.bc, "waves": cfg.waves, "stages": cfg.stages},
-                   "parallelism": "single GPU"},
+                   "heads": w["heads"], "heads_kv": hkv, "d_head": w["d_head"], "causal": causal,
+                   "tile": {"br": cfg.br, "bc": cfg.bc, "waves": cfg.waves, "stages": cfg.stages,
+                            "schedule": cfg.schedule},
+                   "num_splits": splits, "parallelism": "single GPU"},
         "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),

@@ -42,19 +42,42 @@ __global__ void __launch_bounds__(256) fa_merge_kernel(MergeArgs a) {
   const int64_t slab = (int64_t)a.batch * a.heads * a.seqlen_q;  // LSE entries per split
   const int64_t r = ((int64_t)b * a.heads + h) * a.seqlen_q + row;
 
+  // Loads are issued kU splits at a time so that their latencies overlap.  Every split wrote
+  // every row below nq (0 and -inf when it had no visible key), so all reads are defined.
+  constexpr int kU = 8;
+  const int ns = a.num_splits;
+  const float *lp = a.lse_part + r;
+  const float *op = a.o_part + r * D + 4 * c4;
   float mx = -INFINITY;
-  for (int s = 0; s < a.num_splits; ++s) mx = fmaxf(mx, a.lse_part[s * slab + r]);
+  int s = 0;
+  for (; s + kU <= ns; s += kU) {
+    float t[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) t[u] = lp[(s + u) * slab];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) mx = fmaxf(mx, t[u]);
+  }
+  for (; s < ns; ++s) mx = fmaxf(mx, lp[s * slab]);
   float wsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.num_splits; ++s) {
-    const float ls = a.lse_part[s * slab + r];
+  auto add = [&](float ls, const f32x4 &v) {
     const float wgt = __builtin_amdgcn_exp2f((ls - mx) * 1.4426950408889634f);  // 0 for -inf
-    if (wgt > 0.f) {
-      const f32x4 v = *(const f32x4 *)(a.o_part + (s * slab + r) * D + 4 * c4);
-      acc += wgt * v;
-      wsum += wgt;
+    acc += wgt * v;
+    wsum += wgt;
+  };
+  s = 0;
+  for (; s + kU <= ns; s += kU) {
+    float t[kU];
+    f32x4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      t[u] = lp[(s + u) * slab];
+      v[u] = *(const f32x4 *)(op + (s + u) * slab * D);
     }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) add(t[u], v[u]);
   }
+  for (; s < ns; ++s) add(lp[s * slab], *(const f32x4 *)(op + s * slab * D));
   const float inv = 1.f / wsum;
   const int lo = pack2<F16>(acc[0] * inv, acc[1] * inv);
   const int hi = pack2<F16>(acc[2] * inv, acc[3] * inv);

@@ -142,7 +142,7 @@ size_t fa_fwd_workspace_bytes(int batch, int seqlen_q, int n_heads, int d_head, 
 
 /* The split count num_splits = 0 resolves to before the workspace limit:
  * 1 when batch x n_heads x query tiles already gives every CU work, else
- * enough splits for about two workgroups per CU, at most one per two key
+ * enough splits for about two workgroups per CU, at most one per four key
  * tiles and at most FA_MAX_SPLITS.  causal and varlen are 0 or 1.
  * Host-only; < 0 on bad arguments. */
 int fa_fwd_choose_splits(int batch, int seqlen_q, int seqlen_k, int n_heads, int d_head, int dtype,

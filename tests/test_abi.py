@@ -186,8 +186,8 @@ def test_workspace_bytes():
 
 def test_choose_splits():
     # 64 queries over 4096 keys, one head: one workgroup alone -> split, at most one split per
-    # two 64-key tiles
-    assert fa.fa_fwd_choose_splits(1, 64, 4096, 1, 128, fa.FA_BF16) == 32
+    # four 64-key tiles
+    assert fa.fa_fwd_choose_splits(1, 64, 4096, 1, 128, fa.FA_BF16) == 16
     # a grid that already covers the CUs is not split
     assert fa.fa_fwd_choose_splits(16, 4096, 4096, 16, 128, fa.FA_BF16) == 1
     # few keys: no split possible
