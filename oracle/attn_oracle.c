@@ -33,6 +33,15 @@
  *    heads_kv divides heads, and query head h reads K/V head
  *    h / (heads / heads_kv); nothing is copied.
  *
+ * oracle_attention_bwd() is the backward pass of the same page, section 13.1:
+ * with dO given and the scores s_ij = scale <q_i, k_j> (masked as above),
+ *   P = softmax rows, dV = P^T dO, dP_ij = <do_i, v_j>, D_i = sum_j P_ij dP_ij,
+ *   dS_ij = P_ij (dP_ij - D_i), dQ = scale dS K, dK = scale dS^T Q
+ * (the factor scale because the page's S = Q K^T carries no scale here).  D_i is
+ * taken from its definition P_i: . dP_i:, not from the page's simplification
+ * <do_i, o_i> that the GPU path uses.  With grouped K/V heads the dK and dV of
+ * a K/V head sum the contributions of every query head that reads it.
+ *
  * oracle_attention_online() is the second function: the one-pass blockwise
  * recurrence of section 11.2 (two-block merge of (m, l)) and section 11.3
  * (running unnormalised output rescaled by exp(m - m'), divided by l at the
@@ -227,6 +236,90 @@ int oracle_attention_online(const double *q, const double *k, const double *v, d
         }
     free(s);
     free(ot);
+  }
+  return failed ? -1 : 0;
+}
+
+/*
+ * Backward pass (page "GPU 内核与 FlashAttention", section 13.1).  Layouts as in
+ * oracle_attention: q, dout, dq [rows, heads, d]; k, v, dk, dv [rows, heads_kv, d]; dense rows
+ * = batch * n, packed rows = cu[batch].  dq, dk and dv are overwritten.  One OpenMP task per
+ * (sequence, K/V head) owns that head's dk and dv rows, so nothing is shared between threads.
+ * Returns 0, -1 if scratch memory could not be obtained, -2 if heads_kv does not divide heads.
+ */
+int oracle_attention_bwd(const double *q, const double *k, const double *v, const double *dout,
+                         double *dq, double *dk, double *dv, int64_t batch, int64_t nq, int64_t nk,
+                         int64_t heads, int64_t heads_kv, int64_t d, double scale, int causal,
+                         const int64_t *cu) {
+  if (heads_kv <= 0 || heads % heads_kv != 0) return -2;
+  const int64_t group = heads / heads_kv;
+  int64_t max_nk = nk;
+  if (cu) {
+    max_nk = 0;
+    for (int64_t b = 0; b < batch; ++b) if (cu[b + 1] - cu[b] > max_nk) max_nk = cu[b + 1] - cu[b];
+  }
+  int failed = 0;
+#pragma omp parallel
+  {
+    /* per thread: the scores / probabilities of one row and its dP, then dS */
+    double *p = (double *)malloc(sizeof(double) * (size_t)(max_nk > 0 ? max_nk : 1));
+    double *dp = (double *)malloc(sizeof(double) * (size_t)(max_nk > 0 ? max_nk : 1));
+    if (!p || !dp) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for collapse(2) schedule(dynamic, 1)
+    for (int64_t b = 0; b < batch; ++b)
+      for (int64_t hk = 0; hk < heads_kv; ++hk) {
+        if (!p || !dp) continue;
+        int64_t lq = cu ? cu[b + 1] - cu[b] : nq;
+        int64_t lk = cu ? cu[b + 1] - cu[b] : nk;
+        int64_t qrow0 = cu ? cu[b] : b * nq;
+        int64_t krow0 = cu ? cu[b] : b * nk;
+        for (int64_t j = 0; j < lk; ++j)
+          for (int64_t t = 0; t < d; ++t) {
+            dk[at(krow0 + j, hk, t, heads_kv, d)] = 0.0;
+            dv[at(krow0 + j, hk, t, heads_kv, d)] = 0.0;
+          }
+        for (int64_t h = hk * group; h < (hk + 1) * group; ++h)
+          for (int64_t i = 0; i < lq; ++i) {
+            const double *qi = q + at(qrow0 + i, h, 0, heads, d);
+            const double *doi = dout + at(qrow0 + i, h, 0, heads, d);
+            double *dqi = dq + at(qrow0 + i, h, 0, heads, d);
+            /* P_i: = softmax of the (masked) scores */
+            double m = -INFINITY;
+            for (int64_t j = 0; j < lk; ++j) {
+              double acc = 0.0;
+              for (int64_t t = 0; t < d; ++t) acc += qi[t] * k[at(krow0 + j, hk, t, heads_kv, d)];
+              p[j] = (causal && j > i) ? -INFINITY : scale * acc;
+              if (p[j] > m) m = p[j];
+            }
+            double l = 0.0;
+            for (int64_t j = 0; j < lk; ++j) l += exp(p[j] - m);
+            for (int64_t j = 0; j < lk; ++j) p[j] = exp(p[j] - m) / l;
+            /* dP_ij = <do_i, v_j>;  D_i = sum_j P_ij dP_ij */
+            double di = 0.0;
+            for (int64_t j = 0; j < lk; ++j) {
+              double acc = 0.0;
+              for (int64_t t = 0; t < d; ++t) acc += doi[t] * v[at(krow0 + j, hk, t, heads_kv, d)];
+              dp[j] = acc;
+              di += p[j] * acc;
+            }
+            /* dS_ij = P_ij (dP_ij - D_i); dq_i = scale sum_j dS_ij k_j; dk_j += scale dS_ij q_i;
+             * dv_j += P_ij do_i */
+            for (int64_t t = 0; t < d; ++t) dqi[t] = 0.0;
+            for (int64_t j = 0; j < lk; ++j) {
+              double ds = p[j] * (dp[j] - di);
+              for (int64_t t = 0; t < d; ++t) {
+                dqi[t] += scale * ds * k[at(krow0 + j, hk, t, heads_kv, d)];
+                dk[at(krow0 + j, hk, t, heads_kv, d)] += scale * ds * qi[t];
+                dv[at(krow0 + j, hk, t, heads_kv, d)] += p[j] * doi[t];
+              }
+            }
+          }
+      }
+    free(p);
+    free(dp);
   }
   return failed ? -1 : 0;
 }

@@ -55,6 +55,9 @@ def _bind(path):
     lib.oracle_attention_online.restype = ctypes.c_int
     lib.oracle_attention_online.argtypes = [_D, _D, _D, _D, _D, _i64, _i64, _i64, _i64, _i64,
                                             ctypes.c_double, ctypes.c_int, _i64]
+    lib.oracle_attention_bwd.restype = ctypes.c_int
+    lib.oracle_attention_bwd.argtypes = [_D, _D, _D, _D, _D, _D, _D, _i64, _i64, _i64, _i64, _i64, _i64,
+                                         ctypes.c_double, ctypes.c_int, _I64]
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
 
@@ -168,6 +171,33 @@ def attention_online(q, k, v, scale, block, causal=False, _lib_override=None):
     return o, lse
 
 
+def attention_bwd(q, k, v, dout, scale, cu_seqlens=None, max_seqlen=None, causal=False, _lib_override=None):
+    """Gradients of exact attention in fp64 (page "GPU 内核与 FlashAttention", section 13.1).
+
+    Same layouts as attention(); dout is shaped like q.  Returns (dQ like q, dK like k,
+    dV like v).  Packed rows outside every sequence are left 0.
+    """
+    lib = _lib_override or _load()
+    batch, nq, nk, heads, hkv, d, cu = _shapes(np.asarray(q), np.asarray(k), np.asarray(v),
+                                               cu_seqlens, max_seqlen)
+    if np.asarray(dout).shape != np.asarray(q).shape:
+        raise ValueError("dout must be shaped like q")
+    q, qp = _f64(q)
+    k, kp = _f64(k)
+    v, vp = _f64(v)
+    dout, dop = _f64(dout)
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    cup = cu.ctypes.data_as(_I64) if cu is not None else None
+    rc = lib.oracle_attention_bwd(qp, kp, vp, dop, dq.ctypes.data_as(_D), dk.ctypes.data_as(_D),
+                                  dv.ctypes.data_as(_D), batch, nq, nk, heads, hkv, d, float(scale),
+                                  int(bool(causal)), cup)
+    if rc != 0:
+        raise MemoryError("oracle_attention_bwd failed")
+    return dq, dk, dv
+
+
 def num_threads():
     """OpenMP threads the oracle runs with."""
     return int(_load().oracle_num_threads())
@@ -191,6 +221,9 @@ class Oracle:
 
     def attention_online(self, *a, **kw):
         return attention_online(*a, _lib_override=self._lib, **kw)
+
+    def attention_bwd(self, *a, **kw):
+        return attention_bwd(*a, _lib_override=self._lib, **kw)
 
 
 def compile_source(src_text, out_path):

@@ -8,7 +8,8 @@ Sources: page "GPU 内核与 FlashAttention" section 10 (attention as S = QK^T w
 (the blockwise recurrence is exact), section 13.2 (LSE = m + log l), section 14.2
 (grouped K/V heads: several query heads index one K/V head, nothing copied) and
 section 14.4 (causal: scores with j > i are -inf; blocks wholly above the diagonal can
-be skipped without changing the result).
+be skipped without changing the result), section 13.1 (the backward pass: the gradients
+of phi = <dO, O>, which finite differences of the forward oracle must reproduce).
 """
 import json
 import math
@@ -331,10 +332,94 @@ def pin_grouped_heads_are_repeated_heads(orc):
     np.testing.assert_allclose(lse, lse2, rtol=0, atol=1e-14, equal_nan=True)
 
 
+def _loss(orc, q, k, v, dout, scale, **kw):
+    """phi = <dO, O(q, k, v)>: its gradients are what the backward pass returns."""
+    o, _ = orc.attention(q, k, v, scale, **kw)
+    return float(np.sum(dout * o))
+
+
+def _fd_check(orc, q, k, v, dout, scale, rng, n_coords=12, **kw):
+    """Central differences of phi at random coordinates of q, k and v against the backward
+    oracle (step 1e-5: truncation ~1e-10, rounding ~1e-11)."""
+    dq, dk, dv = orc.attention_bwd(q, k, v, dout, scale, **kw)
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(n_coords):
+            idx = tuple(int(rng.integers(n)) for n in x.shape)
+            h = 1e-5
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            fp = _loss(orc, args["q"], args["k"], args["v"], dout, scale, **kw)
+            args[name] = xm
+            fm = _loss(orc, args["q"], args["k"], args["v"], dout, scale, **kw)
+            fd = (fp - fm) / (2 * h)
+            assert abs(fd - g[idx]) <= 1e-7 * max(1.0, abs(fd)), (name, idx, fd, g[idx])
+
+
+def pin_bwd_finite_differences(orc):
+    """The backward oracle's dQ, dK, dV are the gradients of <dO, O>: central differences of
+    the (pinned) forward oracle, plain, causal, grouped heads and packed."""
+    rng = np.random.default_rng(28)
+    q, k, v = _rand(rng, 2, 7, 4, 8), _rand(rng, 2, 9, 4, 8), _rand(rng, 2, 9, 4, 8)
+    dout = _rand(rng, 2, 7, 4, 8)
+    _fd_check(orc, q, k, v, dout, 0.5, rng)
+    _fd_check(orc, q, k, v, dout, 0.5, rng, causal=True)
+    kg, vg = _rand(rng, 2, 9, 2, 8), _rand(rng, 2, 9, 2, 8)
+    _fd_check(orc, q, kg, vg, dout, 0.5, rng)
+    _fd_check(orc, q, kg[:, :, :1].copy(), vg[:, :, :1].copy(), dout, 0.5, rng, causal=True)
+    lens = [3, 1, 6]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    qp, kp, vp, dp = (_rand(rng, 10, 4, 8), _rand(rng, 10, 2, 8), _rand(rng, 10, 2, 8), _rand(rng, 10, 4, 8))
+    _fd_check(orc, qp, kp, vp, dp, 0.5, rng, cu_seqlens=cu, causal=True)
+
+
+def pin_bwd_tiny_all_coordinates(orc):
+    """Every coordinate of a 3-query, 4-key, d 2 causal case by central differences."""
+    rng = np.random.default_rng(29)
+    q, k, v, dout = _rand(rng, 1, 3, 1, 2), _rand(rng, 1, 4, 1, 2), _rand(rng, 1, 4, 1, 2), _rand(rng, 1, 3, 1, 2)
+    for causal in (False, True):
+        _fd_check(orc, q, k, v, dout, 0.9, rng, n_coords=40, causal=causal)
+
+
+def pin_bwd_value_identities(orc):
+    """O is linear in V with rows of P summing to 1: sum_j dV_j = sum_i dO_i (per head), and
+    <dV, V> = <dO, O>.  Shifting every key by one vector leaves O unchanged, so the rows of dK
+    sum to 0 (per head, under the causal mask too)."""
+    rng = np.random.default_rng(30)
+    q, k, v, dout = _rand(rng, 2, 11, 2, 8), _rand(rng, 2, 13, 2, 8), _rand(rng, 2, 13, 2, 8), _rand(rng, 2, 11, 2, 8)
+    for causal in (False, True):
+        dq, dk, dv = orc.attention_bwd(q, k, v, dout, 0.4, causal=causal)
+        np.testing.assert_allclose(dv.sum(axis=1), dout.sum(axis=1), rtol=0, atol=1e-12)
+        o, _ = orc.attention(q, k, v, 0.4, causal=causal)
+        assert abs(np.sum(dv * v) - np.sum(dout * o)) < 1e-11
+        np.testing.assert_allclose(dk.sum(axis=1), 0.0, rtol=0, atol=1e-12)
+
+
+def pin_bwd_identical_keys_and_single_key(orc):
+    """All keys equal: P is uniform (1/Nk), so dV_j = mean_i... = (1/Nk) sum_i dO_i for every j
+    and dQ = 0 (dS rows sum to 0 and multiply one key).  Nk = 1: P = 1, dS = 0, so dQ = dK = 0
+    and dV_0 = sum_i dO_i."""
+    rng = np.random.default_rng(31)
+    nk, d = 6, 8
+    q, dout = _rand(rng, 1, 5, 2, d), _rand(rng, 1, 5, 2, d)
+    k = np.broadcast_to(_rand(rng, 1, 1, 2, d), (1, nk, 2, d)).copy()
+    v = _rand(rng, 1, nk, 2, d)
+    dq, dk, dv = orc.attention_bwd(q, k, v, dout, 0.3)
+    np.testing.assert_allclose(dq, 0.0, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, np.broadcast_to(dout.sum(axis=1, keepdims=True) / nk, dv.shape), rtol=0, atol=1e-12)
+    dq1, dk1, dv1 = orc.attention_bwd(q, k[:, :1], v[:, :1], dout, 0.3)
+    np.testing.assert_allclose(dq1, 0.0, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk1, 0.0, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv1[:, 0], dout.sum(axis=1), rtol=0, atol=1e-12)
+
+
 PINS = [pin_hand_2x2, pin_hand_4x4, pin_values_one, pin_identical_keys, pin_dominant_logit,
         pin_value_identity_is_softmax, pin_single_key, pin_permutations_and_linearity,
         pin_shift_invariance, pin_large_logits, pin_online_recurrence_is_exact,
         pin_varlen_is_per_sequence, pin_rows_match_full, pin_causal_hand_3x3,
         pin_causal_identical_keys, pin_causal_value_identity, pin_causal_is_prefix_attention,
         pin_causal_block_skipping_is_exact, pin_causal_varlen_is_per_sequence,
-        pin_grouped_heads_are_repeated_heads]
+        pin_grouped_heads_are_repeated_heads, pin_bwd_finite_differences, pin_bwd_tiny_all_coordinates,
+        pin_bwd_value_identities, pin_bwd_identical_keys_and_single_key]

@@ -38,6 +38,19 @@ MUTATIONS = {
     "causal_skips_diagonal_block": ("if (causal && j0 > i) break;", "if (causal && j0 + block > i + 1) break;"),
     "causal_online_no_inner_mask": ("if (causal && j0 + jj > i) s[jj] = -INFINITY;", ""),
     "grouped_head_modulo": ("h / group", "h % heads_kv"),
+    "bwd_no_D": ("double ds = p[j] * (dp[j] - di);", "double ds = p[j] * dp[j];"),
+    "bwd_D_sign": ("double ds = p[j] * (dp[j] - di);", "double ds = p[j] * (dp[j] + di);"),
+    "bwd_dk_no_scale": ("dk[at(krow0 + j, hk, t, heads_kv, d)] += scale * ds * qi[t];",
+                        "dk[at(krow0 + j, hk, t, heads_kv, d)] += ds * qi[t];"),
+    "bwd_dq_no_scale": ("dqi[t] += scale * ds * k[at(krow0 + j, hk, t, heads_kv, d)];",
+                        "dqi[t] += ds * k[at(krow0 + j, hk, t, heads_kv, d)];"),
+    "bwd_dv_uses_dp": ("dv[at(krow0 + j, hk, t, heads_kv, d)] += p[j] * doi[t];",
+                       "dv[at(krow0 + j, hk, t, heads_kv, d)] += dp[j] * doi[t];"),
+    "bwd_dp_uses_k": ("for (int64_t t = 0; t < d; ++t) acc += doi[t] * v[at(krow0 + j, hk, t, heads_kv, d)];",
+                      "for (int64_t t = 0; t < d; ++t) acc += doi[t] * k[at(krow0 + j, hk, t, heads_kv, d)];"),
+    "bwd_causal_ignored": ("p[j] = (causal && j > i) ? -INFINITY : scale * acc;", "p[j] = scale * acc;"),
+    "bwd_group_first_head_only": ("for (int64_t h = hk * group; h < (hk + 1) * group; ++h)",
+                                  "for (int64_t h = hk * group; h < hk * group + 1; ++h)"),
 }
 
 
