@@ -1,0 +1,457 @@
+// fa_bwd_kernel.h -- the gfx950 attention backward pass (device code).
+//
+// What it computes (page "GPU 内核与 FlashAttention", section 13): given dO, the gradients
+// of the forward pass O = softmax(scale Q K^T) V,
+//     P = exp(scale Q K^T - L)            (L = the forward's natural-log LSE per row)
+//     dV = P^T dO,   dP = dO V^T,   D = rowsum(dO o O),   dS = P o (dP - D),
+//     dQ = scale dS K,   dK = scale dS^T Q,
+// in the order of that page's blocked backward (section 13.2) and FlashAttention-2's
+// parallelisation (section 14.2): one workgroup per (batch, K/V head, tile of BKV keys)
+// keeps its keys' dK and dV in registers over the whole loop on query tiles, and adds its
+// share of dQ into an fp32 accumulator in HBM with atomic adds.  With grouped K/V heads the
+// loop also runs over every query head of the group, so dK and dV of a K/V head are summed
+// on chip (section 14.2).  Under the causal mask the loop starts at the first query tile
+// that can see the workgroup's first key, and only tiles crossing the diagonal are masked.
+//
+// Three kernels:
+//   fa_bwd_pre_kernel   D_i = <dO_i, O_i> (the page's simplification of P_i . dP_i),
+//                       L_i log2(e) for exp2, and a zeroed dQ accumulator row;
+//   fa_bwd_kernel       the main loop;
+//   fa_bwd_dq_kernel    dQ = 16-bit(scale x accumulator).
+//
+// gfx950 mapping (the forward's building blocks in other roles):
+//  * Each wavefront owns 32 keys.  S = Q K^T and dP = dO V^T are formed with the K and V
+//    rows of its keys held in registers as the B operand (lane = key) and Q / dO rows read
+//    from LDS as the A operand (the forward's qk_block), so in the 32x32 accumulator lane l
+//    holds key l%32 and 16 query rows 8g + 4(l/32) + r.
+//  * Those registers, P and dS rounded to 16 bits, are directly the B operand of
+//    dV^T += dO^T P and dK^T += Q^T dS, whose A operands are read transposed from the
+//    row-major dO and Q tiles with ds_read_b64_tr_b16 (the forward's pv_block, with query
+//    rows in place of key rows).
+//  * dS also goes to LDS as dS^T [key][query]; after a barrier each wavefront forms two
+//    32x32 tiles of dQ = dS K over all the workgroup's keys, both operands read transposed
+//    (dS^T and the resident K tile), and adds them to the accumulator with global atomic
+//    adds (no return value).
+//  * Q, dO, L log2(e) and D of the next query tile stream into LDS (buffer_load ... lds)
+//    while the current one is used.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_bwd.h"
+#include "fa_fwd_kernel.h"
+
+namespace fa {
+
+// ---------------------------------------------------------------------------------------
+// Preprocess: one row (b, i, h) per D/8 lanes, 16-byte loads of O and dO.
+template <int D, bool F16>
+__global__ void __launch_bounds__(256) fa_bwd_pre_kernel(BwdArgs a) {
+  constexpr int LPR = D / 8;      // lanes per row
+  constexpr int RPB = 256 / LPR;  // rows per block
+  const int nchunk = (a.seqlen_q + RPB - 1) / RPB;
+  const int bh = blockIdx.x / nchunk;
+  const int chunk = blockIdx.x % nchunk;
+  const int h = bh % a.heads;
+  const int b = bh / a.heads;
+  int nq;
+  int64_t qrow0;
+  if (a.cu_seqlens) {
+    qrow0 = a.cu_seqlens[b];
+    nq = a.cu_seqlens[b + 1] - a.cu_seqlens[b];
+  } else {
+    nq = a.seqlen_q;
+    qrow0 = (int64_t)b * nq;
+  }
+  const int row = chunk * RPB + (int)threadIdx.x / LPR;
+  const int c8 = threadIdx.x % LPR;
+  float dot = 0.f;
+  const bool valid = row < nq;
+  const int64_t elt = ((qrow0 + row) * a.heads + h) * (int64_t)D + 8 * c8;
+  if (valid) {
+    const i32x4 ov = *(const i32x4 *)((const char *)a.o + elt * 2);
+    const i32x4 dv = *(const i32x4 *)((const char *)a.dout + elt * 2);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // Elements are copied to scalars before __builtin_bit_cast: applied to a vector element
+      // directly, this compiler read element 0 in every iteration.
+      const int oe = ov[e], de = dv[e];
+      f32x2 x, y;
+      if constexpr (F16) {
+        x = __builtin_convertvector(__builtin_bit_cast(f16x2, oe), f32x2);
+        y = __builtin_convertvector(__builtin_bit_cast(f16x2, de), f32x2);
+      } else {
+        x = __builtin_convertvector(__builtin_bit_cast(bf16x2, oe), f32x2);
+        y = __builtin_convertvector(__builtin_bit_cast(bf16x2, de), f32x2);
+      }
+      dot = __builtin_fmaf(x[0], y[0], dot);
+      dot = __builtin_fmaf(x[1], y[1], dot);
+    }
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    *(f32x4 *)(a.dq_acc + elt) = z;
+    *(f32x4 *)(a.dq_acc + elt + 4) = z;
+  }
+  // sum over the LPR lanes of the row (consecutive lanes, LPR a power of two)
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, LPR);
+  if (valid && c8 == 0) {
+    const int64_t r = ((int64_t)b * a.heads + h) * a.seqlen_q + row;
+    a.dvec[r] = dot;
+    a.lse2[r] = a.lse[r] * 1.4426950408889634f;
+  }
+}
+
+// dQ = 16-bit(scale x accumulator), four floats per lane.
+template <int D, bool F16>
+__global__ void __launch_bounds__(256) fa_bwd_dq_kernel(BwdArgs a) {
+  constexpr int LPR = D / 4;
+  constexpr int RPB = 256 / LPR;
+  const int nchunk = (a.seqlen_q + RPB - 1) / RPB;
+  const int bh = blockIdx.x / nchunk;
+  const int chunk = blockIdx.x % nchunk;
+  const int h = bh % a.heads;
+  const int b = bh / a.heads;
+  int nq;
+  int64_t qrow0;
+  if (a.cu_seqlens) {
+    qrow0 = a.cu_seqlens[b];
+    nq = a.cu_seqlens[b + 1] - a.cu_seqlens[b];
+  } else {
+    nq = a.seqlen_q;
+    qrow0 = (int64_t)b * nq;
+  }
+  const int row = chunk * RPB + (int)threadIdx.x / LPR;
+  if (row >= nq) return;
+  const int c4 = threadIdx.x % LPR;
+  const int64_t elt = ((qrow0 + row) * a.heads + h) * (int64_t)D + 4 * c4;
+  const f32x4 x = *(const f32x4 *)(a.dq_acc + elt);
+  const int lo = pack2<F16>(x[0] * a.scale, x[1] * a.scale);
+  const int hi = pack2<F16>(x[2] * a.scale, x[3] * a.scale);
+  *(int2 *)((char *)a.dq + elt * 2) = make_int2(lo, hi);
+}
+
+// ---------------------------------------------------------------------------------------
+// Main kernel.
+
+__device__ __forceinline__ void wait_lds_all() { __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// dQ tile (32 query rows x 32 d) += dS (32 x BKV keys) K (BKV keys x 32 d), both operands read
+// transposed: A from dS^T [key][query] (column = query), B from K [key][d] (column = d).  In a
+// 16-key step lane l supplies keys 16 ks + 4(l/32) + {0..3} and 16 ks + 8 + 4(l/32) + {0..3}
+// of its column, the order the accumulator layout of the other products uses.
+template <int BKV, int AROWB, int BROWB, bool F16, int LA = 3>
+__device__ __forceinline__ void dq_block(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x16 &acc) {
+  constexpr int N = BKV / 16;
+  constexpr int L = LA < N ? LA : N;
+  static_assert(4 * L <= 15, "lgkmcnt field");
+  i16x4 x0[L + 1], x1[L + 1], y0[L + 1], y1[L + 1];
+  auto issue = [&](auto i_c) __attribute__((always_inline)) {
+    constexpr int i = decltype(i_c)::value;  // key step i: rows 16 i + ... of both tiles
+    lds_read_tr<16 * i * AROWB>(x0[i % (L + 1)], a0);
+    lds_read_tr<16 * i * AROWB>(x1[i % (L + 1)], a1);
+    lds_read_tr<16 * i * BROWB>(y0[i % (L + 1)], b0);
+    lds_read_tr<16 * i * BROWB>(y1[i % (L + 1)], b1);
+  };
+  static_for<0, L>(issue);
+  static_for<0, N>([&](auto i_c) __attribute__((always_inline)) {
+    constexpr int i = decltype(i_c)::value;
+    if constexpr (i + L < N) issue(IC<i + L>{});
+    constexpr int after = 4 * ((N - 1 - i) < L ? (N - 1 - i) : L);
+    lds_wait<after>();
+    lds_dep(x0[i % (L + 1)]);
+    lds_dep(x1[i % (L + 1)]);
+    lds_dep(y0[i % (L + 1)]);
+    lds_dep(y1[i % (L + 1)]);
+    const i16x4 &p0 = x0[i % (L + 1)], &p1 = x1[i % (L + 1)], &r0 = y0[i % (L + 1)], &r1 = y1[i % (L + 1)];
+    const i16x8 av = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+    const i16x8 bv = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+    acc = mfma32<F16>(__builtin_bit_cast(i32x4, av), __builtin_bit_cast(i32x4, bv), acc);
+  });
+}
+
+// Store a transposed accumulator tile set (lane = key column l%32, rows d = 32 dt + 8 g +
+// 4(l/32) + r) times mul as 16-bit rows of a [rows, heads_kv, D] tensor, as the forward's
+// output store does; rows past the buffer's range are dropped.
+template <int D, bool F16>
+__device__ __forceinline__ void store_rows(const f32x16 (&A)[D / 32], float mul, int row0, uint32_t row_bytes,
+                                           const __amdgpu_buffer_rsrc_t &rs, int lane) {
+  constexpr int DT = D / 32;
+  const int hi = lane >> 5;
+  const uint32_t off = (uint32_t)(row0 + (lane & 31)) * row_bytes + hi * 16;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int g0 = 2 * p, g1 = 2 * p + 1;
+      const int x0 = pack2<F16>(A[dt][4 * g0 + 0] * mul, A[dt][4 * g0 + 1] * mul);
+      const int x1 = pack2<F16>(A[dt][4 * g0 + 2] * mul, A[dt][4 * g0 + 3] * mul);
+      const int y0 = pack2<F16>(A[dt][4 * g1 + 0] * mul, A[dt][4 * g1 + 1] * mul);
+      const int y1 = pack2<F16>(A[dt][4 * g1 + 2] * mul, A[dt][4 * g1 + 3] * mul);
+      auto s0 = __builtin_amdgcn_permlane32_swap((unsigned)x0, (unsigned)y0, false, false);
+      auto s1 = __builtin_amdgcn_permlane32_swap((unsigned)x1, (unsigned)y1, false, false);
+      const i32x4 out = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+      __builtin_amdgcn_raw_buffer_store_b128(out, rs, off + (32 * dt + 16 * p) * 2, 0, 0);
+    }
+  }
+}
+
+// BKV = 32 * NW keys per workgroup, BQ = 64 query rows per step (two 32-row blocks).
+template <int D, int NW, bool F16>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1)))
+fa_bwd_kernel(BwdArgs a) {
+  constexpr int BKV = 32 * NW;
+  constexpr int BQ = 64;
+  constexpr int QB = BQ / 32;        // 32-row query blocks per step
+  constexpr int ROWB = D * 2;        // bytes of a Q / dO / K row in LDS
+  constexpr int DSROWB = BQ * 2;     // bytes of a dS^T row (one key, BQ queries)
+  constexpr int QT = BQ * ROWB;      // bytes of a Q (or dO) tile
+  constexpr int KT = BKV * ROWB;     // bytes of the K tile
+  constexpr int DST = BKV * DSROWB;  // bytes of the dS^T tile
+  constexpr int VT = BQ * 4;         // bytes of an L log2(e) (or D) row segment
+  // LDS: K tile | dS^T tile | (Q, dO) x 2 stages | (L log2(e), D) x 2 stages
+  constexpr int LDS_BYTES = KT + DST + 4 * QT + 4 * VT;
+  constexpr int DT = D / 32;
+  constexpr int NCHQ = QT / 1024;    // 1 KB pieces of a Q tile
+  constexpr int NCHK = KT / 1024;
+  // dQ output tiles of a step: QB x DT, spread over the wavefronts
+  constexpr int NTILE = QB * DT;
+  constexpr int TPW = NTILE / NW;
+  static_assert(NTILE % NW == 0, "dQ tiles per wavefront");
+  static_assert(NCHQ % NW == 0 && NCHK % NW == 0, "tile pieces per wavefront");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(D == 32 || D == 64 || D == 128, "d_head");
+
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+  char *sk = smem;
+  char *sds = smem + KT;
+  char *sqd = smem + KT + DST;           // stage st: Q at sqd + 2 st QT, dO after it
+  char *svec = smem + KT + DST + 4 * QT;  // stage st: L log2(e) at svec + 2 st VT, D after it
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hi = lane >> 5;
+
+  const int w = blockIdx.x;
+  const int G = a.total_wgs;
+  const int per = G >> 3, rem = G & 7, xcd = w & 7;
+  const int lin = xcd * per + min(xcd, rem) + (w >> 3);
+  const int kt = lin % a.n_ktiles;
+  const int bhk = lin / a.n_ktiles;
+  const int hk = bhk % a.heads_kv;
+  const int b = bhk / a.heads_kv;
+
+  int nq, nk;
+  int64_t qrow0, krow0;
+  if (a.cu_seqlens) {
+    const int s0 = a.cu_seqlens[b], s1 = a.cu_seqlens[b + 1];
+    nq = nk = s1 - s0;
+    qrow0 = krow0 = s0;
+  } else {
+    nq = a.seqlen_q;
+    nk = a.seqlen_k;
+    qrow0 = (int64_t)b * nq;
+    krow0 = (int64_t)b * nk;
+  }
+  const int k0 = kt * BKV;
+  if (k0 >= nk || nq <= 0) return;  // uniform over the workgroup
+
+  const int64_t hd = (int64_t)a.heads * D;
+  const int64_t hkd = (int64_t)a.heads_kv * D;
+  const uint32_t q_row_bytes = (uint32_t)(hd * 2);
+  const uint32_t kv_row_bytes = (uint32_t)(hkd * 2);
+  const char *kb_ = (const char *)a.k + (krow0 * hkd + (int64_t)hk * D) * 2;
+  const char *vb = (const char *)a.v + (krow0 * hkd + (int64_t)hk * D) * 2;
+  const auto rk = make_rsrc(kb_, (uint32_t)(nk - 1) * kv_row_bytes + ROWB);
+  const auto rv = make_rsrc(vb, (uint32_t)(nk - 1) * kv_row_bytes + ROWB);
+
+  // The K tile to LDS (B operand of dQ, read transposed), swizzled like the forward's tiles.
+  auto load_rows = [&](const __amdgpu_buffer_rsrc_t &rsrc, char *dst, int row0, uint32_t row_bytes, int nch)
+                       __attribute__((always_inline)) {
+    for (int u = wave; u < nch; u += NW) {
+      const int pos = u * 1024 + lane * 16;
+      const int r = pos / ROWB;
+      const int cc = ((pos % ROWB) >> 4) ^ swz<D>(r);
+      const uint32_t goff = (uint32_t)(row0 + r) * row_bytes + cc * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void FA_LDS *)(dst + u * 1024), 16, goff, 0, 0, 0);
+    }
+  };
+  load_rows(rk, sk, k0, kv_row_bytes, NCHK);
+
+  // The wavefront's 32 keys in registers: B operand of S = Q K^T (K) and dP = dO V^T (V).
+  const int kw0 = k0 + 32 * wave;
+  const int my_key = kw0 + (lane & 31);
+  i32x4 kreg[D / 16], vreg[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    const uint32_t off = (uint32_t)my_key * kv_row_bytes + (2 * t + hi) * 16;
+    kreg[t] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+    vreg[t] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+  }
+
+  f32x16 dKt[DT], dVt[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dKt[dt] = f32x16{};
+    dVt[dt] = f32x16{};
+  }
+  const LdsAddr ad = lds_addr<D>(lane);
+  const LdsAddr ads = lds_addr<BQ>(lane);  // transposed reads of dS^T (rows of BQ queries)
+  const float c = a.scale_log2;
+
+  // Query tiles: all of them, or under the causal mask those holding a row >= k0.
+  const int nqt = (nq + BQ - 1) / BQ;
+  const int qt0 = a.causal ? min(k0 / BQ, nqt) : 0;
+  const int nqt_w = nqt - qt0;
+  const int n_steps = nqt_w * a.group;  // (query head, query tile) pairs
+
+  // Loads of step s = (head h_of(s), tile qt0 + s % nqt_w) into stage s & 1.
+  auto issue_step = [&](int s) __attribute__((always_inline)) {
+    const int h = hk * a.group + s / nqt_w;
+    const int q0 = (qt0 + s % nqt_w) * BQ;
+    char *st = sqd + (s & 1) * 2 * QT;
+    char *sv = svec + (s & 1) * 2 * VT;
+    const int64_t hoff = (qrow0 * hd + (int64_t)h * D) * 2;
+    const auto rq = make_rsrc((const char *)a.q + hoff, (uint32_t)(nq - 1) * q_row_bytes + ROWB);
+    const auto rdo = make_rsrc((const char *)a.dout + hoff, (uint32_t)(nq - 1) * q_row_bytes + ROWB);
+    load_rows(rq, st, q0, q_row_bytes, NCHQ);
+    load_rows(rdo, st + QT, q0, q_row_bytes, NCHQ);
+    const int64_t vrow = ((int64_t)b * a.heads + h) * a.seqlen_q;
+    if (wave == 0) {
+      const auto rl = make_rsrc(a.lse2 + vrow, (uint32_t)nq * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (void FA_LDS *)sv, 4, (uint32_t)(q0 + lane) * 4, 0, 0, 0);
+    } else if (wave == 1) {
+      const auto rd = make_rsrc(a.dvec + vrow, (uint32_t)nq * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (void FA_LDS *)(sv + VT), 4, (uint32_t)(q0 + lane) * 4, 0, 0, 0);
+    }
+  };
+
+  if (n_steps > 0) issue_step(0);
+  // vmcnt bookkeeping: a step's loads are followed (in issue order) only by the next step's
+  // loads and by this step's dQ atomics, TPW x 16 per lane.
+  constexpr int NATOM = TPW * 16;
+  static_assert(NATOM + 2 * (NCHQ / NW) + 1 <= 63, "vmcnt field");
+
+  for (int s = 0; s < n_steps; ++s) {
+    // Step s's loads (and, before them, the K tile and registers) have landed once at most
+    // the previous step's atomics are still in flight.
+    if (s == 0)
+      wait_vmcnt<0>();
+    else
+      wait_vmcnt<NATOM>();
+    wg_barrier();  // everyone's loads landed; everyone is done with stage (s+1)&1 and dS^T
+    if (s + 1 < n_steps) issue_step(s + 1);
+
+    const int h = hk * a.group + s / nqt_w;
+    const int q0 = (qt0 + s % nqt_w) * BQ;
+    const char *sq = sqd + (s & 1) * 2 * QT;
+    const char *sdo = sq + QT;
+    const float *sl2 = (const float *)(svec + (s & 1) * 2 * VT);
+    const float *sdv = sl2 + BQ;
+
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      f32x16 S[1], dP[1];
+      qk_block<D, 32, F16>(sq + qb * 32 * ROWB, S, kreg, ad);
+      qk_block<D, 32, F16>(sdo + qb * 32 * ROWB, dP, vreg, ad);
+      // rows of this lane: query q0 + 32 qb + 8 g + 4 hi + r
+      const int rb = 32 * qb + 4 * hi;
+      f32x4 l2[4], dd[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        l2[g] = *(const f32x4 *)(sl2 + rb + 8 * g);
+        dd[g] = *(const f32x4 *)(sdv + rb + 8 * g);
+      }
+      // masked: key past the sequence, or (causal) key past the query
+      const int qrow_base = q0 + rb;
+      i32x4 Pp[2], dSp[2];
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = 4 * g + r;
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[0][e], c, -l2[g][r]));
+          const bool masked = my_key >= nk || (a.causal && my_key > qrow_base + 8 * g + r);
+          p = masked ? 0.f : p;
+          pv[e] = p;
+          dsv[e] = p * (dP[0][e] - dd[g][r]);
+        }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          Pp[s2][e] = pack2<F16>(pv[8 * s2 + 2 * e], pv[8 * s2 + 2 * e + 1]);
+          dSp[s2][e] = pack2<F16>(dsv[8 * s2 + 2 * e], dsv[8 * s2 + 2 * e + 1]);
+        }
+      // dS^T [key][query] for the dQ product: lane's key row, queries 32 qb + 8 g + 4 hi + 0..3
+      {
+        const int kr = 32 * wave + (lane & 31);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = 32 * qb + 8 * g + 4 * hi;  // 4 queries = 8 bytes, half a 16-byte chunk
+          const int chunk = (col >> 3) ^ swz<BQ>(kr);
+          const int2 val = make_int2(dSp[g >> 1][2 * (g & 1)], dSp[g >> 1][2 * (g & 1) + 1]);
+          *(int2 *)(sds + kr * DSROWB + chunk * 16 + (col & 7) * 2) = val;
+        }
+      }
+      pv_block<D, 32, F16>(sdo + qb * 32 * ROWB, Pp, dVt, ad);
+      pv_block<D, 32, F16>(sq + qb * 32 * ROWB, dSp, dKt, ad);
+    }
+    wait_lds_all();
+    wg_barrier();  // dS^T complete
+
+    // dQ tiles of this wavefront: tile id = wave * TPW + u -> (query block, d tile).  The
+    // adds go through a buffer resource bounding this head's rows below nq, so every lane
+    // issues the same number of atomics (rows past the end are dropped by the hardware) and
+    // the vmcnt bookkeeping above stays exact.  No cache-policy bits: the same instruction
+    // the compiler emits for a device-scope relaxed float atomic add.
+    const auto rdq = make_rsrc(a.dq_acc + (qrow0 * a.heads + h) * (int64_t)D,
+                               (uint32_t)(nq - 1) * (uint32_t)(hd * 4) + D * 4);
+    const uint32_t sk_lds = (uint32_t)(uintptr_t)(const char FA_LDS *)sk;
+    const uint32_t sds_lds = (uint32_t)(uintptr_t)(const char FA_LDS *)sds;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int tile = wave * TPW + u;
+      const int qbt = tile / DT, dt = tile % DT;
+      f32x16 acc = f32x16{};
+      const uint32_t a0 = sds_lds + (uint32_t)(((64 * qbt) ^ ads.vx0) + ads.vbase0);
+      const uint32_t a1 = sds_lds + (uint32_t)(((64 * qbt) ^ ads.vx1) + ads.vbase1);
+      const uint32_t b0 = sk_lds + (uint32_t)(((64 * dt) ^ ad.vx0) + ad.vbase0);
+      const uint32_t b1 = sk_lds + (uint32_t)(((64 * dt) ^ ad.vx1) + ad.vbase1);
+      dq_block<BKV, DSROWB, ROWB, F16>(a0, a1, b0, b1, acc);
+      // lane holds d = 32 dt + l%32 of query rows q0 + 32 qbt + 8 g + 4 hi + r
+      const uint32_t base = (uint32_t)(q0 + 32 * qbt + 4 * hi) * (uint32_t)(hd * 4) + (32 * dt + (lane & 31)) * 4;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[4 * g + r], rdq,
+                                                          base + (uint32_t)(8 * g + r) * (uint32_t)(hd * 4), 0, 0);
+    }
+  }
+
+  // dK = scale dS^T Q and dV = P^T dO of this wavefront's 32 keys.
+  const auto rdk = make_rsrc((char *)a.dk + (krow0 * hkd + (int64_t)hk * D) * 2, (uint32_t)(nk - 1) * kv_row_bytes + ROWB);
+  const auto rdv = make_rsrc((char *)a.dv + (krow0 * hkd + (int64_t)hk * D) * 2, (uint32_t)(nk - 1) * kv_row_bytes + ROWB);
+  store_rows<D, F16>(dKt, a.scale, kw0, kv_row_bytes, rdk, lane);
+  store_rows<D, F16>(dVt, 1.f, kw0, kv_row_bytes, rdv, lane);
+}
+
+template <int D, int NW, bool F16>
+hipError_t launch_fa_bwd(const BwdArgs &a, hipStream_t stream) {
+  BwdArgs arg = a;
+  void *args[] = {&arg};
+  constexpr int RPB_PRE = 256 / (D / 8);
+  constexpr int RPB_DQ = 256 / (D / 4);
+  const int bh = a.batch * a.heads;
+  hipError_t e = hipLaunchKernel((const void *)&fa_bwd_pre_kernel<D, F16>,
+                                 dim3(bh * ((a.seqlen_q + RPB_PRE - 1) / RPB_PRE)), dim3(256), args, 0, stream);
+  if (e != hipSuccess) return e;
+  e = hipLaunchKernel((const void *)&fa_bwd_kernel<D, NW, F16>, dim3(a.total_wgs), dim3(NW * 64), args, 0, stream);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel((const void *)&fa_bwd_dq_kernel<D, F16>, dim3(bh * ((a.seqlen_q + RPB_DQ - 1) / RPB_DQ)),
+                         dim3(256), args, 0, stream);
+}
+
+}  // namespace fa

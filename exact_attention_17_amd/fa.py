@@ -15,7 +15,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_MISALIGNED, FA_ERR_HIP = 0
 FA_MAX_SPLITS = 128
 
 # Every exported symbol of include/fa_fwd.h.
-EXPORTS = ("fa_fwd", "fa_fwd_ext", "fa_fwd_workspace_bytes", "fa_fwd_choose_splits",
+EXPORTS = ("fa_fwd", "fa_fwd_ext", "fa_fwd_workspace_bytes", "fa_fwd_choose_splits", "fa_bwd",
+           "fa_bwd_workspace_bytes",
            "fa_fwd_autotune", "fa_fwd_set_config", "fa_fwd_get_config", "fa_fwd_num_configs", "fa_fwd_list_configs", "fa_fwd_config_lds_bytes",
            "fa_fwd_config_resources", "fa_last_error", "fa_version")
 
@@ -62,6 +63,11 @@ def lib():
         L.fa_fwd_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
         L.fa_fwd_choose_splits.restype = _i
         L.fa_fwd_choose_splits.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
+        L.fa_bwd.restype = _i
+        L.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, ctypes.c_float,
+                             _i, _vp, _i, _vp, ctypes.c_size_t, _vp]
+        L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.fa_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i]
         L.fa_fwd_autotune.restype = _i
         L.fa_fwd_autotune.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.c_float, _vp,
                                       _i, _vp, _i, ctypes.POINTER(TileConfig),
@@ -213,6 +219,43 @@ def fa_fwd_ext(q, k, v, o=None, lse=None, scale=None, causal=False, cu_seqlens=N
                           int(num_splits), ws_ptr, ws_bytes, _stream_handle(stream, q.device))
     _check(st)
     return o, lse
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq=None, dk=None, dv=None, scale=None, causal=False, cu_seqlens=None,
+           max_seqlen=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of the forward pass given its output o and lse and dout = dPhi/dO.
+    Shapes as in fa_fwd_ext (k and v may have fewer heads); dout like q.  A workspace of
+    fa_bwd_workspace_bytes(...) bytes is allocated with torch when none is given."""
+    import torch
+    batch, nq, nk, heads, heads_kv, d = _shape_args(q, k, v, cu_seqlens, max_seqlen, grouped=True)
+    _check_tensors(q, k, v, cu_seqlens)
+    for t in (o, dout):
+        if not t.is_cuda or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("o and dout must be contiguous device tensors shaped and typed like q")
+    if not lse.is_cuda or lse.dtype != torch.float32 or tuple(lse.shape) != (batch, heads, nq):
+        raise ValueError("lse must be a float32 device tensor [batch, n_heads, seqlen_q]")
+    if scale is None:
+        scale = d ** -0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(fa_bwd_workspace_bytes(batch, nq, heads, d), dtype=torch.uint8, device=q.device)
+    st = lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), batch, nq, nk, heads, heads_kv, d, float(scale),
+                      int(bool(causal)), cu_seqlens.data_ptr() if cu_seqlens is not None else None,
+                      _dtype_code(q), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                      _stream_handle(stream, q.device))
+    _check(st)
+    return dq, dk, dv
+
+
+def fa_bwd_workspace_bytes(batch, seqlen_q, n_heads, d_head):
+    """Workspace bytes fa_bwd needs."""
+    n = lib().fa_bwd_workspace_bytes(batch, seqlen_q, n_heads, d_head)
+    if n == 0:
+        raise FaError(FA_ERR_INVALID_ARG, fa_last_error())
+    return n
 
 
 def fa_fwd_workspace_bytes(batch, seqlen_q, n_heads, d_head, num_splits):

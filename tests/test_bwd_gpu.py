@@ -1,0 +1,119 @@
+"""GPU parity of the backward pass (fa_bwd) against the fp64 oracle's gradients.
+
+The forward output O and LSE come from the library's own forward pass (as in training);
+dO is seeded N(0,1) rounded to the 16-bit type.  The oracle recomputes everything in fp64
+from the same 16-bit Q, K, V and dO.
+
+Bar (derived from the 16-bit roundings of P, dS, O and the outputs): for each of dQ, dK,
+dV, max-abs error <= 2e-2 x max|reference| + 1e-4 and mean-abs error <= 1e-2 x
+mean|reference| + 1e-5.  The absolute terms cover gradients whose exact value is 0 (one
+key, identical keys): there the GPU result is the rounding of D = <dO, O> computed from the
+16-bit O, of order |dO| |O| 2^-8 / sqrt(d) per query row.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_17_amd import fa, inputs
+
+pytestmark = pytest.mark.gpu
+
+REL_MAX, REL_MEAN = 2e-2, 1e-2
+ABS_MAX, ABS_MEAN = 1e-4, 1e-5
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def dout_like(q, seed):
+    g = torch.Generator().manual_seed(int(seed))
+    return torch.randn(q.shape, generator=g, dtype=torch.float32).to(q.dtype)
+
+
+def run_bwd(q, k, v, do, scale, causal=False, cu=None, max_seqlen=None):
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    cud = cu.to(dev) if cu is not None else None
+    o, lse = fa.fa_fwd_ext(qd, kd, vd, scale=scale, causal=causal, cu_seqlens=cud, max_seqlen=max_seqlen)
+    dq, dk, dv = fa.fa_bwd(qd, kd, vd, o, lse, dod, scale=scale, causal=causal, cu_seqlens=cud,
+                           max_seqlen=max_seqlen)
+    torch.cuda.synchronize()
+    return [t.cpu().to(torch.float64).numpy() for t in (dq, dk, dv)]
+
+
+def compare(got, want, what):
+    bad = []
+    for name, g, w in zip(("dQ", "dK", "dV"), got, want):
+        err = np.abs(g - w)
+        ref_max, ref_mean = np.abs(w).max(), np.abs(w).mean()
+        say("%s %s: max err %.3g (ref max %.3g, ratio %.2e)  mean err %.3g (ref mean %.3g, ratio %.2e)"
+            % (what, name, err.max(), ref_max, err.max() / max(ref_max, 1e-30), err.mean(), ref_mean,
+               err.mean() / max(ref_mean, 1e-30)))
+        if not (np.all(np.isfinite(g)) and err.max() <= REL_MAX * ref_max + ABS_MAX
+                and err.mean() <= REL_MEAN * ref_mean + ABS_MEAN):
+            bad.append(name)
+    assert not bad, (what, bad)
+
+
+def check_dense(b, nq, nk, h, hkv, d, dtype, causal, seed):
+    q, k, v = inputs.dense_qkv(b, nq, nk, h, d, dtype, seed=seed, heads_kv=hkv)
+    do = dout_like(q, seed + 1000)
+    scale = d ** -0.5
+    what = "bwd B%d nq%d nk%d H%d Hkv%d d%d %s causal=%d" % (b, nq, nk, h, hkv, d, dtype, causal)
+    say("case " + what)
+    got = run_bwd(q, k, v, do, scale, causal=causal)
+    want = oracle.attention_bwd(*(inputs.to_f64(t) for t in (q, k, v, do)), scale, causal=causal)
+    compare(got, want, what)
+
+
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "bf16"), (32, "bf16"), (128, "fp16"), (64, "fp16"),
+                                     (32, "fp16")])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_square(d, dtype, causal):
+    check_dense(2, 256, 256, 2, 2, d, dtype, causal, seed=d + causal)
+
+
+@pytest.mark.parametrize("nq,nk", [(1, 1), (63, 63), (65, 130), (300, 100), (100, 300), (129, 257), (2, 3)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_ragged(nq, nk, causal):
+    check_dense(1, nq, nk, 3, 3, 128, "bf16", causal, seed=nq + 7 * nk)
+
+
+@pytest.mark.parametrize("hkv", [1, 2])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_grouped_heads(hkv, causal):
+    check_dense(2, 200, 200, 4, hkv, 64, "bf16", causal, seed=50 + hkv)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_varlen(causal):
+    lengths = [1, 130, 0, 64, 300, 77]
+    q, k, v, cu, max_len = inputs.varlen_qkv(heads=4, d_head=128, dtype="bf16", seed=61, lengths=lengths,
+                                             heads_kv=2)
+    do = dout_like(q, 62)
+    scale = 128 ** -0.5
+    what = "bwd varlen %s causal=%d" % (lengths, causal)
+    say("case " + what)
+    got = run_bwd(q, k, v, do, scale, causal=causal, cu=cu, max_seqlen=max_len)
+    want = oracle.attention_bwd(*(inputs.to_f64(t) for t in (q, k, v, do)), scale, cu_seqlens=cu.numpy(),
+                                max_seqlen=max_len, causal=causal)
+    compare(got, want, what)
+
+
+def test_bwd_longer_sequence():
+    check_dense(1, 1024, 1024, 2, 2, 128, "bf16", True, seed=71)
+    check_dense(1, 1024, 1024, 2, 1, 128, "bf16", False, seed=72)
