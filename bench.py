@@ -13,6 +13,11 @@ Other modes (used to produce the committed profiles and the secondary measuremen
                         causal, gqa); causal counts only the visible (query, key) pairs
     --splits N          key-range splits per query tile (fa_fwd_ext num_splits): 0 = the
                         library's automatic choice (default), 1 = no split
+    --pass bwd          time the backward pass (fa_bwd: preprocess, main and dQ kernels) on
+                        the workload instead, with O and LSE from one forward call and a
+                        seeded dO; FLOPs counted as 2.5x the forward's (five products
+                        instead of two, the pages' convention)
+    --atomic-dq         with --pass bwd: dQ by atomic adds instead of the separate dQ pass
     --copy-bytes N      run only a plain device copy of N bytes (the counter calibration)
     --no-cpu-baseline   skip the oracle timing
 """
@@ -142,6 +147,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="full")
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd")
+    ap.add_argument("--atomic-dq", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -194,6 +201,22 @@ def main():
         fa.fa_fwd_ext(qd, kd, vd, o, lse, scale=w["scale"], causal=causal, cu_seqlens=cu,
                       max_seqlen=w["max_seqlen"], num_splits=splits, workspace=workspace, stream=stream)
 
+    if args.which == "bwd":
+        step()  # O and LSE of this workload
+        g = torch.Generator().manual_seed(int(w["seed"]) + 1000)
+        dout = torch.randn(tuple(qd.shape), generator=g, dtype=torch.float32).to(qd.dtype).to(dev)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        bws = torch.empty(fa.fa_bwd_workspace_bytes(w["batch"], w["seqlen_q"], w["heads"], w["d_head"],
+                                                    args.atomic_dq), dtype=torch.uint8, device=dev)
+        flops = flops * 5 // 2
+        # algorithmic bytes: Q, K, V, O, dO read and dQ, dK, dV written (16-bit), LSE read and
+        # D, L log2(e) written once (fp32 per query row)
+        nbytes = 2 * nbytes + 2 * 4 * qd.numel() // w["d_head"]
+
+        def step():  # noqa: F811
+            fa.fa_bwd(qd, kd, vd, o, lse, dout, dq, dk, dv, scale=w["scale"], causal=causal, cu_seqlens=cu,
+                      max_seqlen=w["max_seqlen"], atomic_dq=args.atomic_dq, workspace=bws, stream=stream)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -208,20 +231,21 @@ def main():
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / args.steps
     tflops = flops / (ms * 1e-3) / 1e12
-    log("%s: %.4f ms per step (wall %.4f ms), %.1f TFLOP/s, %.1f%% of %.1f, tiles %r, splits %d"
-        % (args.workload, ms, wall * 1e3 / args.steps, tflops, 100 * tflops / PEAK_BF16_TFLOPS,
+    log("%s %s: %.4f ms per step (wall %.4f ms), %.1f TFLOP/s, %.1f%% of %.1f, tiles %r, splits %d"
+        % (args.workload, args.which, ms, wall * 1e3 / args.steps, tflops, 100 * tflops / PEAK_BF16_TFLOPS,
            PEAK_BF16_TFLOPS, cfg, splits))
 
-    traffic = read_traffic(args.workload)
+    traffic = read_traffic(args.workload) if args.which == "fwd" else None
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.which == "fwd":
         log("timing the fp64 oracle on a bounded sample")
         cpu = cpu_baseline(w)
         log("oracle: %.3g TFLOP/s on %d threads (%s)" % (cpu["value"], cpu["cores"], cpu["sample"]))
 
     wl = WORKLOAD_NAMES[args.workload]
-    metric = HEADLINE_METRIC if args.workload == "full" else \
-        "fwd TFLOP/s (4 d x visible query-key pairs per batch and head) on %s; %% of MFMA bf16 peak" % wl
+    metric = HEADLINE_METRIC if args.workload == "full" and args.which == "fwd" else \
+        "%s TFLOP/s (%s x 4 d x visible query-key pairs per batch and head) on %s; %% of MFMA bf16 peak" % (
+            args.which, "2.5" if args.which == "bwd" else "1", wl)
     out = {
         "metric": metric,
         "value": round(tflops, 2),
@@ -239,7 +263,8 @@ def main():
                    "heads": w["heads"], "heads_kv": hkv, "d_head": w["d_head"], "causal": causal,
                    "tile": {"br": cfg.br, "bc": cfg.bc, "waves": cfg.waves, "stages": cfg.stages,
                             "schedule": cfg.schedule},
-                   "num_splits": splits, "parallelism": "single GPU"},
+                   "num_splits": splits, "pass": args.which,
+                   "atomic_dq": bool(args.atomic_dq) if args.which == "bwd" else None, "parallelism": "single GPU"},
         "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),

@@ -18,7 +18,8 @@ struct BwdArgs {
   int total_wgs;  // batch * heads_kv * n_ktiles
   float scale;
   float scale_log2;  // scale * log2(e)
-  float *dq_acc;     // [rows, heads, D] fp32; rows = batch * seqlen_q (packed: token rows)
+  float *dq_acc;     // [rows, heads, D] fp32, rows = batch * seqlen_q (packed: token rows), for
+                     // dQ by atomic adds; nullptr = dQ by the separate pass
   float *dvec;       // [batch, heads, seqlen_q]: D_i = <dO_i, O_i>
   float *lse2;       // [batch, heads, seqlen_q]: L_i log2(e)
 };

@@ -88,9 +88,11 @@ __global__ void __launch_bounds__(256) fa_bwd_pre_kernel(BwdArgs a) {
       dot = __builtin_fmaf(x[0], y[0], dot);
       dot = __builtin_fmaf(x[1], y[1], dot);
     }
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    *(f32x4 *)(a.dq_acc + elt) = z;
-    *(f32x4 *)(a.dq_acc + elt + 4) = z;
+    if (a.dq_acc) {  // the atomic path accumulates dQ here
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      *(f32x4 *)(a.dq_acc + elt) = z;
+      *(f32x4 *)(a.dq_acc + elt + 4) = z;
+    }
   }
   // sum over the LPR lanes of the row (consecutive lanes, LPR a power of two)
 #pragma unroll
@@ -197,7 +199,9 @@ __device__ __forceinline__ void store_rows(const f32x16 (&A)[D / 32], float mul,
 }
 
 // BKV = 32 * NW keys per workgroup, BQ = 64 query rows per step (two 32-row blocks).
-template <int D, int NW, bool F16>
+// ATOMIC_DQ: also form dQ = dS K here and add it into the fp32 accumulator with atomics (the
+// pages' Algorithm 2); otherwise dQ is left to fa_bwd_dq_pass_kernel.
+template <int D, int NW, bool F16, bool ATOMIC_DQ>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1)))
 fa_bwd_kernel(BwdArgs a) {
   constexpr int BKV = 32 * NW;
@@ -205,15 +209,15 @@ fa_bwd_kernel(BwdArgs a) {
   constexpr int QB = BQ / 32;        // 32-row query blocks per step
   constexpr int ROWB = D * 2;        // bytes of a Q / dO / K row in LDS
   constexpr int DSROWB = BQ * 2;     // bytes of a dS^T row (one key, BQ queries)
-  constexpr int QT = BQ * ROWB;      // bytes of a Q (or dO) tile
-  constexpr int KT = BKV * ROWB;     // bytes of the K tile
-  constexpr int DST = BKV * DSROWB;  // bytes of the dS^T tile
+  constexpr int QT = BQ * ROWB;                   // bytes of a Q (or dO) tile
+  constexpr int KT = ATOMIC_DQ ? BKV * ROWB : 0;  // bytes of the K tile (dQ product only)
+  constexpr int DST = ATOMIC_DQ ? BKV * DSROWB : 0;  // bytes of the dS^T tile (dQ product only)
   constexpr int VT = BQ * 4;         // bytes of an L log2(e) (or D) row segment
   // LDS: K tile | dS^T tile | (Q, dO) x 2 stages | (L log2(e), D) x 2 stages
   constexpr int LDS_BYTES = KT + DST + 4 * QT + 4 * VT;
   constexpr int DT = D / 32;
   constexpr int NCHQ = QT / 1024;    // 1 KB pieces of a Q tile
-  constexpr int NCHK = KT / 1024;
+  constexpr int NCHK = BKV * ROWB / 1024;
   // dQ output tiles of a step: QB x DT, spread over the wavefronts
   constexpr int NTILE = QB * DT;
   constexpr int TPW = NTILE / NW;
@@ -276,7 +280,7 @@ fa_bwd_kernel(BwdArgs a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void FA_LDS *)(dst + u * 1024), 16, goff, 0, 0, 0);
     }
   };
-  load_rows(rk, sk, k0, kv_row_bytes, NCHK);
+  if constexpr (ATOMIC_DQ) load_rows(rk, sk, k0, kv_row_bytes, NCHK);
 
   // The wavefront's 32 keys in registers: B operand of S = Q K^T (K) and dP = dO V^T (V).
   const int kw0 = k0 + 32 * wave;
@@ -329,7 +333,7 @@ fa_bwd_kernel(BwdArgs a) {
   if (n_steps > 0) issue_step(0);
   // vmcnt bookkeeping: a step's loads are followed (in issue order) only by the next step's
   // loads and by this step's dQ atomics, TPW x 16 per lane.
-  constexpr int NATOM = TPW * 16;
+  constexpr int NATOM = ATOMIC_DQ ? TPW * 16 : 0;
   static_assert(NATOM + 2 * (NCHQ / NW) + 1 <= 63, "vmcnt field");
 
   for (int s = 0; s < n_steps; ++s) {
@@ -385,7 +389,7 @@ fa_bwd_kernel(BwdArgs a) {
           dSp[s2][e] = pack2<F16>(dsv[8 * s2 + 2 * e], dsv[8 * s2 + 2 * e + 1]);
         }
       // dS^T [key][query] for the dQ product: lane's key row, queries 32 qb + 8 g + 4 hi + 0..3
-      {
+      if constexpr (ATOMIC_DQ) {
         const int kr = 32 * wave + (lane & 31);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -398,6 +402,7 @@ fa_bwd_kernel(BwdArgs a) {
       pv_block<D, 32, F16>(sdo + qb * 32 * ROWB, Pp, dVt, ad);
       pv_block<D, 32, F16>(sq + qb * 32 * ROWB, dSp, dKt, ad);
     }
+    if constexpr (ATOMIC_DQ) {
     wait_lds_all();
     wg_barrier();  // dS^T complete
 
@@ -429,6 +434,7 @@ fa_bwd_kernel(BwdArgs a) {
           __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[4 * g + r], rdq,
                                                           base + (uint32_t)(8 * g + r) * (uint32_t)(hd * 4), 0, 0);
     }
+    }  // ATOMIC_DQ
   }
 
   // dK = scale dS^T Q and dV = P^T dO of this wavefront's 32 keys.
@@ -438,7 +444,163 @@ fa_bwd_kernel(BwdArgs a) {
   store_rows<D, F16>(dVt, 1.f, kw0, kv_row_bytes, rdv, lane);
 }
 
-template <int D, int NW, bool F16>
+// ---------------------------------------------------------------------------------------
+// The dQ pass (when dQ is not accumulated with atomics): the forward's structure with query
+// rows owned by wavefronts and K/V tiles streamed through LDS, and the products
+//     S^T = K Q^T,  dP^T = V dO^T   (K, V rows from LDS; Q, dO in registers, lane = query)
+//     P = exp2(S c - L log2 e),  dS = P o (dP - D)   (L, D one value per lane)
+//     dQ^T += K^T dS^T              (K read transposed; dS registers as the B operand)
+// so dQ is summed over every key on chip and written once: no accumulator, no atomics,
+// the same bits on every run.  No running max or rescale: P is final given L.
+template <int D, int BC, int NW, bool F16>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+fa_bwd_dq_pass_kernel(BwdArgs a) {
+  constexpr int BR = 32 * NW;
+  constexpr int ROWB = D * 2;
+  constexpr int TILE = BC * ROWB;
+  constexpr int NCH = TILE / 1024;
+  constexpr int DT = D / 32;
+  constexpr int KB = BC / 32;
+  constexpr int KS = BC / 16;
+  constexpr int STAGE = 2 * TILE;  // K tile then V tile
+  constexpr int LPT = 2 * (NCH >= NW ? NCH / NW : 1);
+  static_assert(NCH % NW == 0 || NW % NCH == 0, "tile pieces spread evenly");
+  static_assert(2 * STAGE <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hi = lane >> 5;
+  const int n_qtiles = (a.seqlen_q + BR - 1) / BR;
+
+  const int w = blockIdx.x;
+  const int G = a.batch * a.heads * n_qtiles;
+  const int per = G >> 3, rem = G & 7, xcd = w & 7;
+  const int lin = xcd * per + min(xcd, rem) + (w >> 3);
+  const int qi = lin % n_qtiles;
+  const int qt = a.causal ? n_qtiles - 1 - qi : qi;
+  const int bh = lin / n_qtiles;
+  const int h = bh % a.heads;
+  const int b = bh / a.heads;
+  const int hk = h / a.group;
+
+  int nq, nk;
+  int64_t qrow0, krow0;
+  if (a.cu_seqlens) {
+    const int s0 = a.cu_seqlens[b], s1 = a.cu_seqlens[b + 1];
+    nq = nk = s1 - s0;
+    qrow0 = krow0 = s0;
+  } else {
+    nq = a.seqlen_q;
+    nk = a.seqlen_k;
+    qrow0 = (int64_t)b * nq;
+    krow0 = (int64_t)b * nk;
+  }
+  const int q_tile0 = qt * BR;
+  if (q_tile0 >= nq || nk <= 0) return;
+
+  const int64_t hd = (int64_t)a.heads * D;
+  const int64_t hkd = (int64_t)a.heads_kv * D;
+  const uint32_t row_bytes = (uint32_t)(hd * 2);
+  const uint32_t kv_row_bytes = (uint32_t)(hkd * 2);
+  const int64_t qoff = (qrow0 * hd + (int64_t)h * D) * 2;
+  const auto rq = make_rsrc((const char *)a.q + qoff, (uint32_t)(nq - 1) * row_bytes + ROWB);
+  const auto rdo = make_rsrc((const char *)a.dout + qoff, (uint32_t)(nq - 1) * row_bytes + ROWB);
+  const auto rdq = make_rsrc((char *)a.dq + qoff, (uint32_t)(nq - 1) * row_bytes + ROWB);
+  const int64_t kvoff = (krow0 * hkd + (int64_t)hk * D) * 2;
+  const auto rk = make_rsrc((const char *)a.k + kvoff, (uint32_t)(nk - 1) * kv_row_bytes + ROWB);
+  const auto rv = make_rsrc((const char *)a.v + kvoff, (uint32_t)(nk - 1) * kv_row_bytes + ROWB);
+
+  const int wrow0 = q_tile0 + wave * 32;
+  const int my_row = wrow0 + (lane & 31);
+  i32x4 qreg[D / 16], doreg[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    const uint32_t off = (uint32_t)my_row * row_bytes + (2 * t + hi) * 16;
+    qreg[t] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+    doreg[t] = __builtin_amdgcn_raw_buffer_load_b128(rdo, off, 0, 0);
+  }
+  // L log2(e) and D of this lane's row (rows past nq: 0, their dQ is not stored)
+  const int64_t vrow = ((int64_t)b * a.heads + h) * a.seqlen_q;
+  const auto rl = make_rsrc(a.lse2 + vrow, (uint32_t)nq * 4);
+  const auto rd = make_rsrc(a.dvec + vrow, (uint32_t)nq * 4);
+  // (the b32 load returns the raw bits as an integer)
+  const float l2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)my_row * 4, 0, 0));
+  const float dd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, (uint32_t)my_row * 4, 0, 0));
+
+  auto load_one = [&](const __amdgpu_buffer_rsrc_t &rsrc, char *dst, int j) __attribute__((always_inline)) {
+    const uint32_t tile_off = (uint32_t)(j * BC) * kv_row_bytes;
+#pragma unroll
+    for (int i = 0; i < (NCH + NW - 1) / NW; ++i) {
+      const int u = wave + i * NW;
+      if (NCH % NW == 0 || u < NCH) {
+        const int pos = u * 1024 + lane * 16;
+        const int r = pos / ROWB;
+        const int cc = ((pos % ROWB) >> 4) ^ swz<D>(r);
+        const uint32_t goff = tile_off + (uint32_t)r * kv_row_bytes + cc * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void FA_LDS *)(dst + u * 1024), 16, goff, 0, 0, 0);
+      }
+    }
+  };
+
+  f32x16 dQt[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dQt[dt] = f32x16{};
+  const float c = a.scale_log2;
+  const LdsAddr ad = lds_addr<D>(lane);
+  const int kend = a.causal ? min(nk, q_tile0 + BR) : nk;
+  const int nkt = (kend + BC - 1) / BC;
+  // visible keys of this lane's row: below klim; tiles below kfull need no mask for the wavefront
+  const int klim = a.causal ? min(nk, my_row + 1) : nk;
+  const int kfull = (a.causal ? min(nk, wrow0 + 1) : nk) / BC;
+  const int wave_kend = a.causal ? min(nk, wrow0 + 32) : nk;
+
+  auto step = [&](auto st_c, int j) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st_c)::value;
+    wait_vmcnt<0>();
+    wg_barrier();
+    if (j + 1 < nkt) {
+      constexpr int NS = ST ^ 1;
+      load_one(rk, smem + NS * STAGE, j + 1);
+      load_one(rv, smem + NS * STAGE + TILE, j + 1);
+    }
+    if (j * BC < wave_kend) {
+      f32x16 S[KB], dP[KB];
+      qk_block<D, BC, F16>(smem + ST * STAGE, S, qreg, ad);
+      qk_block<D, BC, F16>(smem + ST * STAGE + TILE, dP, doreg, ad);
+      // key of register r in block kb: j BC + 32 kb + 8 (r / 4) + 4 hi + r % 4
+      const bool need_mask = j >= kfull;
+      i32x4 dSp[KS];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        float dsv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], c, -l2));
+          if (need_mask && j * BC + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3) >= klim) p = 0.f;
+          dsv[r] = p * (dP[kb][r] - dd);
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dSp[2 * kb + s2][e] = pack2<F16>(dsv[8 * s2 + 2 * e], dsv[8 * s2 + 2 * e + 1]);
+      }
+      pv_block<D, BC, F16>(smem + ST * STAGE, dSp, dQt, ad);
+    }
+  };
+  if (nkt > 0) {
+    load_one(rk, smem, 0);
+    load_one(rv, smem + TILE, 0);
+  }
+  for (int j = 0; j < nkt; j += 2) {
+    step(IC<0>{}, j);
+    if (j + 1 < nkt) step(IC<1>{}, j + 1);
+  }
+  (void)LPT;
+  store_rows<D, F16>(dQt, a.scale, wrow0, row_bytes, rdq, lane);
+}
+
+template <int D, int NW, bool F16, bool ATOMIC_DQ>
 hipError_t launch_fa_bwd(const BwdArgs &a, hipStream_t stream) {
   BwdArgs arg = a;
   void *args[] = {&arg};
@@ -448,10 +610,21 @@ hipError_t launch_fa_bwd(const BwdArgs &a, hipStream_t stream) {
   hipError_t e = hipLaunchKernel((const void *)&fa_bwd_pre_kernel<D, F16>,
                                  dim3(bh * ((a.seqlen_q + RPB_PRE - 1) / RPB_PRE)), dim3(256), args, 0, stream);
   if (e != hipSuccess) return e;
-  e = hipLaunchKernel((const void *)&fa_bwd_kernel<D, NW, F16>, dim3(a.total_wgs), dim3(NW * 64), args, 0, stream);
+  e = hipLaunchKernel((const void *)&fa_bwd_kernel<D, NW, F16, ATOMIC_DQ>, dim3(a.total_wgs), dim3(NW * 64), args, 0,
+                      stream);
   if (e != hipSuccess) return e;
-  return hipLaunchKernel((const void *)&fa_bwd_dq_kernel<D, F16>, dim3(bh * ((a.seqlen_q + RPB_DQ - 1) / RPB_DQ)),
-                         dim3(256), args, 0, stream);
+  if constexpr (ATOMIC_DQ) {
+    return hipLaunchKernel((const void *)&fa_bwd_dq_kernel<D, F16>, dim3(bh * ((a.seqlen_q + RPB_DQ - 1) / RPB_DQ)),
+                           dim3(256), args, 0, stream);
+  } else {
+    // eight wavefronts (256 query rows) at d_head 128 with 32-key tiles, which keeps the
+    // pass within 256 registers per lane (two wavefronts per SIMD) without spilling
+    constexpr int NWQ = D == 128 ? 8 : 4;
+    constexpr int BCQ = D == 128 ? 32 : 64;
+    constexpr int BRQ = 32 * NWQ;
+    return hipLaunchKernel((const void *)&fa_bwd_dq_pass_kernel<D, BCQ, NWQ, F16>,
+                           dim3(bh * ((a.seqlen_q + BRQ - 1) / BRQ)), dim3(NWQ * 64), args, 0, stream);
+  }
 }
 
 }  // namespace fa

@@ -263,6 +263,12 @@ int lds_bytes_of(int d, const fa_tile_config_t &c) {
   return c.schedule == 1 ? 5 * tile : c.stages * 2 * tile;
 }
 
+// Backward workspace: D and L log2(e) per query row, and the fp32 dQ accumulator when dQ is
+// formed with atomic adds.
+size_t bwd_bytes(int batch, int seqlen_q, int n_heads, int d_head, int atomic_dq) {
+  return (size_t)batch * (size_t)seqlen_q * (size_t)n_heads * (size_t)((atomic_dq ? d_head : 0) + 2) * 4u;
+}
+
 }  // namespace
 
 extern "C" {
@@ -328,9 +334,9 @@ int fa_fwd_choose_splits(int batch, int seqlen_q, int seqlen_k, int n_heads, int
   return choose_splits(batch, seqlen_q, seqlen_k, n_heads, d_head, dtype, causal != 0, varlen != 0);
 }
 
-size_t fa_bwd_workspace_bytes(int batch, int seqlen_q, int n_heads, int d_head) {
-  if (batch < 1 || seqlen_q < 1 || n_heads < 1) {
-    fail(FA_ERR_INVALID_ARG, "batch, seqlen_q and n_heads must be >= 1");
+size_t fa_bwd_workspace_bytes(int batch, int seqlen_q, int n_heads, int d_head, int atomic_dq) {
+  if (batch < 1 || seqlen_q < 1 || n_heads < 1 || (atomic_dq != 0 && atomic_dq != 1)) {
+    fail(FA_ERR_INVALID_ARG, "batch, seqlen_q and n_heads must be >= 1 and atomic_dq 0 or 1");
     return 0;
   }
   if (!valid_d(d_head)) {
@@ -338,25 +344,26 @@ size_t fa_bwd_workspace_bytes(int batch, int seqlen_q, int n_heads, int d_head) 
     return 0;
   }
   ok();
-  return (size_t)batch * (size_t)seqlen_q * (size_t)n_heads * (size_t)(d_head + 2) * 4u;
+  return bwd_bytes(batch, seqlen_q, n_heads, d_head, atomic_dq);
 }
 
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse,
            void *dq, void *dk, void *dv, int batch, int seqlen_q, int seqlen_k, int n_heads, int n_heads_kv,
-           int d_head, float scale, int causal, const int32_t *cu_seqlens, int dtype, void *workspace,
-           size_t workspace_bytes, void *stream) {
-  // o and dq stand in for the forward's o in the common checks; dout, dk, dv, workspace below
+           int d_head, float scale, int causal, const int32_t *cu_seqlens, int dtype, int atomic_dq,
+           void *workspace, size_t workspace_bytes, void *stream) {
+  // dq stands in for the forward's o in the common checks; o, dout, dk, dv, workspace below
   int st = check_args(q, k, v, dq, const_cast<float *>(lse), batch, seqlen_q, seqlen_k, n_heads, n_heads_kv,
                       d_head, scale, causal, cu_seqlens, dtype);
   if (st != FA_OK) return st;
   if (!o || !dout || !dk || !dv) return fail(FA_ERR_INVALID_ARG, "o, dout, dk and dv must be non-null");
+  if (atomic_dq != 0 && atomic_dq != 1) return fail(FA_ERR_INVALID_ARG, "atomic_dq must be 0 or 1");
   auto mis = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) % 16) != 0; };
   if (mis(o) || mis(dout) || mis(dk) || mis(dv))
     return fail(FA_ERR_MISALIGNED, "o, dout, dq, dk and dv must be 16-byte aligned");
   if (!workspace) return fail(FA_ERR_INVALID_ARG, "the backward pass needs a workspace");
   if (mis(workspace)) return fail(FA_ERR_MISALIGNED, "workspace must be 16-byte aligned");
-  const size_t need = (size_t)batch * (size_t)seqlen_q * (size_t)n_heads * (size_t)(d_head + 2) * 4u;
-  if (workspace_bytes < need) return fail(FA_ERR_INVALID_ARG, "workspace smaller than fa_bwd_workspace_bytes()");
+  if (workspace_bytes < bwd_bytes(batch, seqlen_q, n_heads, d_head, atomic_dq))
+    return fail(FA_ERR_INVALID_ARG, "workspace smaller than fa_bwd_workspace_bytes()");
   // the fp32 dQ rows of one sequence are addressed with 32-bit offsets (one query tile of slack)
   if (((int64_t)seqlen_q + 64) * n_heads * d_head * 4 >= (int64_t)INT32_MAX)
     return fail(FA_ERR_UNSUPPORTED, "seqlen_q x n_heads x d_head too large for 32-bit offsets");
@@ -385,8 +392,8 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   float *ws = static_cast<float *>(workspace);
   const size_t rows = (size_t)batch * seqlen_q * n_heads;
-  a.dq_acc = ws;
-  a.dvec = ws + rows * d_head;
+  a.dq_acc = atomic_dq ? ws : nullptr;
+  a.dvec = ws + (atomic_dq ? rows * d_head : 0);
   a.lse2 = a.dvec + rows;
   hipError_t err = fa::launch_bwd(a, d_head, dtype, reinterpret_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("backward launch failed: ") + hipGetErrorString(err));

@@ -65,9 +65,9 @@ def lib():
         L.fa_fwd_choose_splits.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
         L.fa_bwd.restype = _i
         L.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, ctypes.c_float,
-                             _i, _vp, _i, _vp, ctypes.c_size_t, _vp]
+                             _i, _vp, _i, _i, _vp, ctypes.c_size_t, _vp]
         L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
-        L.fa_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i]
+        L.fa_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
         L.fa_fwd_autotune.restype = _i
         L.fa_fwd_autotune.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.c_float, _vp,
                                       _i, _vp, _i, ctypes.POINTER(TileConfig),
@@ -222,9 +222,10 @@ def fa_fwd_ext(q, k, v, o=None, lse=None, scale=None, causal=False, cu_seqlens=N
 
 
 def fa_bwd(q, k, v, o, lse, dout, dq=None, dk=None, dv=None, scale=None, causal=False, cu_seqlens=None,
-           max_seqlen=None, workspace=None, stream=None):
+           max_seqlen=None, atomic_dq=False, workspace=None, stream=None):
     """Gradients (dq, dk, dv) of the forward pass given its output o and lse and dout = dPhi/dO.
-    Shapes as in fa_fwd_ext (k and v may have fewer heads); dout like q.  A workspace of
+    Shapes as in fa_fwd_ext (k and v may have fewer heads); dout like q.  atomic_dq selects dQ
+    by atomic adds (the pages' Algorithm 2) instead of the separate dQ pass.  A workspace of
     fa_bwd_workspace_bytes(...) bytes is allocated with torch when none is given."""
     import torch
     batch, nq, nk, heads, heads_kv, d = _shape_args(q, k, v, cu_seqlens, max_seqlen, grouped=True)
@@ -240,19 +241,20 @@ def fa_bwd(q, k, v, o, lse, dout, dq=None, dk=None, dv=None, scale=None, causal=
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     if workspace is None:
-        workspace = torch.empty(fa_bwd_workspace_bytes(batch, nq, heads, d), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(fa_bwd_workspace_bytes(batch, nq, heads, d, atomic_dq), dtype=torch.uint8,
+                                device=q.device)
     st = lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), batch, nq, nk, heads, heads_kv, d, float(scale),
                       int(bool(causal)), cu_seqlens.data_ptr() if cu_seqlens is not None else None,
-                      _dtype_code(q), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                      _stream_handle(stream, q.device))
+                      _dtype_code(q), int(bool(atomic_dq)), workspace.data_ptr(),
+                      workspace.numel() * workspace.element_size(), _stream_handle(stream, q.device))
     _check(st)
     return dq, dk, dv
 
 
-def fa_bwd_workspace_bytes(batch, seqlen_q, n_heads, d_head):
+def fa_bwd_workspace_bytes(batch, seqlen_q, n_heads, d_head, atomic_dq=False):
     """Workspace bytes fa_bwd needs."""
-    n = lib().fa_bwd_workspace_bytes(batch, seqlen_q, n_heads, d_head)
+    n = lib().fa_bwd_workspace_bytes(batch, seqlen_q, n_heads, d_head, int(bool(atomic_dq)))
     if n == 0:
         raise FaError(FA_ERR_INVALID_ARG, fa_last_error())
     return n

@@ -149,33 +149,40 @@ int fa_fwd_choose_splits(int batch, int seqlen_q, int seqlen_k, int n_heads, int
                          int causal, int varlen);
 
 /* Backward pass (page "GPU 内核与 FlashAttention", section 13; FlashAttention-2's
- * parallelisation over K/V tiles with atomic dQ, section 14.2).  Given the
- * forward's inputs, its output o and natural-log lse (from fa_fwd or
- * fa_fwd_ext with the same arguments) and dout = dPhi/dO, writes
+ * parallelisation over K/V tiles, section 14.2).  Given the forward's inputs,
+ * its output o and natural-log lse (from fa_fwd or fa_fwd_ext with the same
+ * arguments) and dout = dPhi/dO, writes
  *   dq = dPhi/dq, dk = dPhi/dk, dv = dPhi/dv
  * with P = exp(scale q k^T - lse), dV = P^T dO, dP = dO V^T,
  * D = rowsum(dO o O), dS = P o (dP - D), dQ = scale dS K, dK = scale dS^T Q.
  * Layouts, n_heads_kv, causal and cu_seqlens as in fa_fwd_ext: dout, dq like
  * q; dk, dv like k.  With grouped K/V heads dk and dv of a K/V head sum the
- * contributions of all its query heads.  The 16-bit outputs are rounded
- * once from fp32; dQ accumulates in fp32 in the workspace with atomic adds,
- * so its bits may vary from run to run in the last place.
+ * contributions of all its query heads.  16-bit outputs are rounded once
+ * from fp32.
+ * atomic_dq selects how dQ is formed:
+ *   0: a second pass over query tiles recomputes S, P, dP and dS and sums
+ *      dQ on chip (no atomics; the same bits on every run);
+ *   1: the pages' Algorithm 2: the K/V-tile pass adds its share of dQ into
+ *      an fp32 accumulator in the workspace with atomic adds (dQ's last bit
+ *      may then vary from run to run).
  * workspace: device memory of at least fa_bwd_workspace_bytes(batch,
- * seqlen_q, n_heads, d_head) bytes, 16-byte aligned, caller-owned (the fp32
- * dQ accumulator and two fp32 values per query row); contents irrelevant
- * before and after.  Enqueued on `stream` (three kernels).  Argument checks
- * as in fa_fwd_ext, plus non-null o, dout, dq, dk, dv (16-byte aligned) and
- * workspace.  Returns an fa_status_t. */
+ * seqlen_q, n_heads, d_head, atomic_dq) bytes, 16-byte aligned,
+ * caller-owned; contents irrelevant before and after.  Enqueued on `stream`
+ * (three kernels).  Argument checks as in fa_fwd_ext, plus non-null o, dout,
+ * dq, dk, dv (16-byte aligned) and workspace; atomic_dq must be 0 or 1.
+ * Returns an fa_status_t. */
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
            const float *lse, void *dq, void *dk, void *dv, int batch, int seqlen_q, int seqlen_k,
            int n_heads, int n_heads_kv, int d_head, float scale, int causal,
-           const int32_t *cu_seqlens, int dtype, void *workspace, size_t workspace_bytes,
-           void *stream);
+           const int32_t *cu_seqlens, int dtype, int atomic_dq, void *workspace,
+           size_t workspace_bytes, void *stream);
 
-/* Workspace bytes fa_bwd needs: batch x seqlen_q x n_heads x (d_head + 2) x 4
- * (packed layout: seqlen_q is the longest length).  0 with fa_last_error()
- * set on bad arguments.  Host-only. */
-size_t fa_bwd_workspace_bytes(int batch, int seqlen_q, int n_heads, int d_head);
+/* Workspace bytes fa_bwd needs: batch x seqlen_q x n_heads x 2 x 4 (D and
+ * L log2(e) per query row), plus batch x seqlen_q x n_heads x d_head x 4 for
+ * the fp32 dQ accumulator when atomic_dq is 1 (packed layout: seqlen_q is
+ * the longest length).  0 with fa_last_error() set on bad arguments.
+ * Host-only. */
+size_t fa_bwd_workspace_bytes(int batch, int seqlen_q, int n_heads, int d_head, int atomic_dq);
 
 /* Tile autotuner (page "Flash Attention 2 Chapter6", Kernel 7: enumerate the
  * configuration space, drop configurations that spill registers or do not

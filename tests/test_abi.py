@@ -206,3 +206,31 @@ def test_ext_binding_refuses_cpu_tensors():
     k = torch.zeros(1, 8, 2, 32, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.fa_fwd_ext(q, k, k, causal=True)
+
+
+def test_bwd_workspace_bytes_and_bad_arguments():
+    assert fa.fa_bwd_workspace_bytes(2, 100, 4, 64) == 2 * 100 * 4 * 2 * 4
+    assert fa.fa_bwd_workspace_bytes(2, 100, 4, 64, atomic_dq=True) == 2 * 100 * 4 * 66 * 4
+    with pytest.raises(fa.FaError):
+        fa.fa_bwd_workspace_bytes(2, 100, 4, 80)
+    L = fa.lib()
+    base = dict(q=A, k=A, v=A, o=A, dout=A, lse=A, dq=A, dk=A, dv=A, batch=1, seqlen_q=128, seqlen_k=128,
+                n_heads=4, n_heads_kv=2, d_head=64, scale=0.125, causal=0, cu=None, dtype=fa.FA_BF16, atomic_dq=0,
+                ws=A, ws_bytes=1 << 30, stream=None)
+
+    def call_bwd(**over):
+        a = dict(base, **over)
+        return L.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"], a["batch"],
+                        a["seqlen_q"], a["seqlen_k"], a["n_heads"], a["n_heads_kv"], a["d_head"],
+                        ctypes.c_float(a["scale"]), a["causal"], a["cu"], a["dtype"], a["atomic_dq"], a["ws"],
+                        a["ws_bytes"], a["stream"])
+    for over, status in ((dict(o=None), fa.FA_ERR_INVALID_ARG), (dict(dout=None), fa.FA_ERR_INVALID_ARG),
+                         (dict(dq=None), fa.FA_ERR_INVALID_ARG), (dict(dk=None), fa.FA_ERR_INVALID_ARG),
+                         (dict(dv=None), fa.FA_ERR_INVALID_ARG), (dict(ws=None), fa.FA_ERR_INVALID_ARG),
+                         (dict(ws=A + 4), fa.FA_ERR_MISALIGNED), (dict(dk=A + 2), fa.FA_ERR_MISALIGNED),
+                         (dict(ws_bytes=128 * 4 * 2 * 4 - 1), fa.FA_ERR_INVALID_ARG),
+                         (dict(atomic_dq=1, ws_bytes=128 * 4 * 2 * 4), fa.FA_ERR_INVALID_ARG),
+                         (dict(atomic_dq=2), fa.FA_ERR_INVALID_ARG), (dict(n_heads_kv=3), fa.FA_ERR_INVALID_ARG),
+                         (dict(causal=5), fa.FA_ERR_INVALID_ARG), (dict(d_head=48), fa.FA_ERR_UNSUPPORTED)):
+        assert call_bwd(**over) == status, over
+        assert fa.fa_last_error() != ""

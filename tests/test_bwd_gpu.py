@@ -44,13 +44,13 @@ def dout_like(q, seed):
     return torch.randn(q.shape, generator=g, dtype=torch.float32).to(q.dtype)
 
 
-def run_bwd(q, k, v, do, scale, causal=False, cu=None, max_seqlen=None):
+def run_bwd(q, k, v, do, scale, causal=False, cu=None, max_seqlen=None, atomic_dq=False):
     dev = torch.device("cuda:0")
     qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
     cud = cu.to(dev) if cu is not None else None
     o, lse = fa.fa_fwd_ext(qd, kd, vd, scale=scale, causal=causal, cu_seqlens=cud, max_seqlen=max_seqlen)
     dq, dk, dv = fa.fa_bwd(qd, kd, vd, o, lse, dod, scale=scale, causal=causal, cu_seqlens=cud,
-                           max_seqlen=max_seqlen)
+                           max_seqlen=max_seqlen, atomic_dq=atomic_dq)
     torch.cuda.synchronize()
     return [t.cpu().to(torch.float64).numpy() for t in (dq, dk, dv)]
 
@@ -69,15 +69,17 @@ def compare(got, want, what):
     assert not bad, (what, bad)
 
 
-def check_dense(b, nq, nk, h, hkv, d, dtype, causal, seed):
+def check_dense(b, nq, nk, h, hkv, d, dtype, causal, seed, modes=(False, True)):
     q, k, v = inputs.dense_qkv(b, nq, nk, h, d, dtype, seed=seed, heads_kv=hkv)
     do = dout_like(q, seed + 1000)
     scale = d ** -0.5
-    what = "bwd B%d nq%d nk%d H%d Hkv%d d%d %s causal=%d" % (b, nq, nk, h, hkv, d, dtype, causal)
-    say("case " + what)
-    got = run_bwd(q, k, v, do, scale, causal=causal)
     want = oracle.attention_bwd(*(inputs.to_f64(t) for t in (q, k, v, do)), scale, causal=causal)
-    compare(got, want, what)
+    for atomic in modes:
+        what = "bwd B%d nq%d nk%d H%d Hkv%d d%d %s causal=%d atomic_dq=%d" % (b, nq, nk, h, hkv, d, dtype, causal,
+                                                                          atomic)
+        say("case " + what)
+        got = run_bwd(q, k, v, do, scale, causal=causal, atomic_dq=atomic)
+        compare(got, want, what)
 
 
 @pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "bf16"), (32, "bf16"), (128, "fp16"), (64, "fp16"),
@@ -106,12 +108,22 @@ def test_bwd_varlen(causal):
                                              heads_kv=2)
     do = dout_like(q, 62)
     scale = 128 ** -0.5
-    what = "bwd varlen %s causal=%d" % (lengths, causal)
-    say("case " + what)
-    got = run_bwd(q, k, v, do, scale, causal=causal, cu=cu, max_seqlen=max_len)
     want = oracle.attention_bwd(*(inputs.to_f64(t) for t in (q, k, v, do)), scale, cu_seqlens=cu.numpy(),
                                 max_seqlen=max_len, causal=causal)
-    compare(got, want, what)
+    for atomic in (False, True):
+        what = "bwd varlen %s causal=%d atomic_dq=%d" % (lengths, causal, atomic)
+        say("case " + what)
+        got = run_bwd(q, k, v, do, scale, causal=causal, cu=cu, max_seqlen=max_len, atomic_dq=atomic)
+        compare(got, want, what)
+
+
+def test_bwd_separate_dq_pass_is_deterministic():
+    q, k, v = inputs.dense_qkv(1, 700, 700, 4, 128, "bf16", seed=81, heads_kv=2)
+    do = dout_like(q, 82)
+    a = run_bwd(q, k, v, do, 128 ** -0.5, causal=True)
+    b = run_bwd(q, k, v, do, 128 ** -0.5, causal=True)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
 
 
 def test_bwd_longer_sequence():
