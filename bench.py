@@ -231,7 +231,7 @@ def main():
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / args.steps
     tflops = flops / (ms * 1e-3) / 1e12
-    log("%s %s: %.4f ms per step (wall %.4f ms), %.1f TFLOP/s, %.1f%% of %.1f, tiles %r, splits %d"
+    log("%s %s: %.4f ms per step (wall %.4f ms), %.1f TFLOP/s, %.1f%% of %.1f, forward tiles %r, splits %d"
         % (args.workload, args.which, ms, wall * 1e3 / args.steps, tflops, 100 * tflops / PEAK_BF16_TFLOPS,
            PEAK_BF16_TFLOPS, cfg, splits))
 
@@ -261,8 +261,10 @@ def main():
         "data": "synthetic (seeded N(0,1), rounded to %s)" % w["dtype"],
         "config": {"workload": wl, "batch": w["batch"], "seq_len_q": w["seqlen_q"], "seq_len_k": w["seqlen_k"],
                    "heads": w["heads"], "heads_kv": hkv, "d_head": w["d_head"], "causal": causal,
-                   "tile": {"br": cfg.br, "bc": cfg.bc, "waves": cfg.waves, "stages": cfg.stages,
-                            "schedule": cfg.schedule},
+                   "tile": ({"br": cfg.br, "bc": cfg.bc, "waves": cfg.waves, "stages": cfg.stages,
+                             "schedule": cfg.schedule} if args.which == "fwd" else
+                            {"dkdv_keys_per_workgroup": 64 if w["d_head"] == 32 else 128,
+                             "dq_pass_rows_per_workgroup": 256 if w["d_head"] == 128 else 128}),
                    "num_splits": splits, "pass": args.which,
                    "atomic_dq": bool(args.atomic_dq) if args.which == "bwd" else None, "parallelism": "single GPU"},
         "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
