@@ -240,10 +240,11 @@ fa_bwd_kernel(BwdArgs a) {
   const int G = a.total_wgs;
   const int per = G >> 3, rem = G & 7, xcd = w & 7;
   const int lin = xcd * per + min(xcd, rem) + (w >> 3);
+  // head-major, as in the forward: every XCD gets a share of every (packed) sequence
   const int kt = lin % a.n_ktiles;
-  const int bhk = lin / a.n_ktiles;
-  const int hk = bhk % a.heads_kv;
-  const int b = bhk / a.heads_kv;
+  const int hkb = lin / a.n_ktiles;
+  const int b = hkb % a.batch;
+  const int hk = hkb / a.batch;
 
   int nq, nk;
   int64_t qrow0, krow0;
@@ -479,9 +480,9 @@ fa_bwd_dq_pass_kernel(BwdArgs a) {
   const int lin = xcd * per + min(xcd, rem) + (w >> 3);
   const int qi = lin % n_qtiles;
   const int qt = a.causal ? n_qtiles - 1 - qi : qi;
-  const int bh = lin / n_qtiles;
-  const int h = bh % a.heads;
-  const int b = bh / a.heads;
+  const int hb = lin / n_qtiles;  // head-major, as in the forward
+  const int b = hb % a.batch;
+  const int h = hb / a.batch;
   const int hk = h / a.group;
 
   int nq, nk;

@@ -33,7 +33,8 @@
 //    (16 B per lane, 32 rows) and the transposed V reads (8 B per lane,
 //    8 rows x 4 chunks) spread over all banks.
 //  * Workgroups are renumbered so that the query tiles of one (batch, head)
-//    run on the same XCD and share its L2 for K/V.
+//    run on the same XCD and share its L2 for K/V; an XCD's range runs over
+//    heads first, so every XCD gets a share of every (packed) sequence.
 //
 // Three schedules:
 //  SCHED 0: each wavefront owns one 32-row block and runs QK^T, softmax and
@@ -466,9 +467,12 @@ fa_fwd_kernel(FaArgs a) {
   const int qi = lt % a.n_qtiles;
   // under the causal mask the work of a query tile grows with its index: start the longest
   const int qt = a.causal ? a.n_qtiles - 1 - qi : qi;
-  const int bh = lt / a.n_qtiles;
-  const int h = bh % a.heads;
-  const int b = bh / a.heads;
+  // head-major: an XCD's contiguous range covers a few heads of every sequence, so packed
+  // sequences of different lengths spread evenly over the XCDs, while the query tiles of one
+  // (sequence, head) stay together and share that XCD's L2 for their K/V
+  const int hb = lt / a.n_qtiles;
+  const int b = hb % a.batch;
+  const int h = hb / a.batch;
   const int hk = h / a.group;  // the K/V head this query head reads
 
   int nq, nk;
