@@ -202,7 +202,7 @@ __device__ __forceinline__ void store_rows(const f32x16 (&A)[D / 32], float mul,
 // ATOMIC_DQ: also form dQ = dS K here and add it into the fp32 accumulator with atomics (the
 // pages' Algorithm 2); otherwise dQ is left to fa_bwd_dq_pass_kernel.
 template <int D, int NW, bool F16, bool ATOMIC_DQ>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ATOMIC_DQ ? 1 : 2)))
 fa_bwd_kernel(BwdArgs a) {
   constexpr int BKV = 32 * NW;
   constexpr int BQ = 64;
@@ -357,38 +357,36 @@ fa_bwd_kernel(BwdArgs a) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       f32x16 S[1], dP[1];
-      qk_block<D, 32, F16>(sq + qb * 32 * ROWB, S, kreg, ad);
-      qk_block<D, 32, F16>(sdo + qb * 32 * ROWB, dP, vreg, ad);
-      // rows of this lane: query q0 + 32 qb + 8 g + 4 hi + r
+      // (shorter read lookahead than the forward's: two wavefronts per SIMD hide latency and
+      // the registers are needed for dK and dV)
+      qk_block<D, 32, F16, 3>(sq + qb * 32 * ROWB, S, kreg, ad);
+      qk_block<D, 32, F16, 3>(sdo + qb * 32 * ROWB, dP, vreg, ad);
+      // rows of this lane: query q0 + 32 qb + 8 g + 4 hi + r; L log2(e) and D are read from
+      // LDS four rows at a time, and P and dS packed to 16 bits as they are formed
       const int rb = 32 * qb + 4 * hi;
-      f32x4 l2[4], dd[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        l2[g] = *(const f32x4 *)(sl2 + rb + 8 * g);
-        dd[g] = *(const f32x4 *)(sdv + rb + 8 * g);
-      }
-      // masked: key past the sequence, or (causal) key past the query
       const int qrow_base = q0 + rb;
       i32x4 Pp[2], dSp[2];
-      float pv[16], dsv[16];
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 l2 = *(const f32x4 *)(sl2 + rb + 8 * g);
+        const f32x4 dd = *(const f32x4 *)(sdv + rb + 8 * g);
+        float pv[4], dsv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int e = 4 * g + r;
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[0][e], c, -l2[g][r]));
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[0][e], c, -l2[r]));
+          // masked: key past the sequence, or (causal) key past the query
           const bool masked = my_key >= nk || (a.causal && my_key > qrow_base + 8 * g + r);
           p = masked ? 0.f : p;
-          pv[e] = p;
-          dsv[e] = p * (dP[0][e] - dd[g][r]);
+          pv[r] = p;
+          dsv[r] = p * (dP[0][e] - dd[r]);
         }
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          Pp[s2][e] = pack2<F16>(pv[8 * s2 + 2 * e], pv[8 * s2 + 2 * e + 1]);
-          dSp[s2][e] = pack2<F16>(dsv[8 * s2 + 2 * e], dsv[8 * s2 + 2 * e + 1]);
-        }
+        // register e = 4g + r of step s2 = g / 2, dword (g % 2) * 2 + r / 2
+        Pp[g >> 1][2 * (g & 1)] = pack2<F16>(pv[0], pv[1]);
+        Pp[g >> 1][2 * (g & 1) + 1] = pack2<F16>(pv[2], pv[3]);
+        dSp[g >> 1][2 * (g & 1)] = pack2<F16>(dsv[0], dsv[1]);
+        dSp[g >> 1][2 * (g & 1) + 1] = pack2<F16>(dsv[2], dsv[3]);
+      }
       // dS^T [key][query] for the dQ product: lane's key row, queries 32 qb + 8 g + 4 hi + 0..3
       if constexpr (ATOMIC_DQ) {
         const int kr = 32 * wave + (lane & 31);
@@ -400,8 +398,8 @@ fa_bwd_kernel(BwdArgs a) {
           *(int2 *)(sds + kr * DSROWB + chunk * 16 + (col & 7) * 2) = val;
         }
       }
-      pv_block<D, 32, F16>(sdo + qb * 32 * ROWB, Pp, dVt, ad);
-      pv_block<D, 32, F16>(sq + qb * 32 * ROWB, dSp, dKt, ad);
+      pv_block<D, 32, F16, 2>(sdo + qb * 32 * ROWB, Pp, dVt, ad);
+      pv_block<D, 32, F16, 2>(sq + qb * 32 * ROWB, dSp, dKt, ad);
     }
     if constexpr (ATOMIC_DQ) {
     wait_lds_all();
