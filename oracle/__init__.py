@@ -5,5 +5,5 @@ tests/, the smoke check in __graft_entry__ and the CPU-baseline leg of bench.py
 may import it.  It shares no code with the HIP library and the library never
 calls it.
 """
-from .oracle import (Oracle, attention, attention_bwd, attention_online, attention_rows,  # noqa: F401
-                     build, compile_source, library_path, num_threads, source_text)
+from .oracle import (Oracle, attention, attention_bwd, attention_bwd_rows, attention_online,  # noqa: F401
+                     attention_rows, build, compile_source, library_path, num_threads, source_text)

@@ -324,6 +324,162 @@ int oracle_attention_bwd(const double *q, const double *k, const double *v, cons
   return failed ? -1 : 0;
 }
 
+/*
+ * Row statistics of query row i of head h (section 13.1): fills p[j] = P_ij over the lk keys
+ * (0 above the diagonal when causal), dp[j] = <do_i, v_j>, and returns D_i = sum_j P_ij dP_ij;
+ * *lse_out = m + log l.
+ */
+static double bwd_row(const double *q, const double *k, const double *v, const double *dout,
+                      int64_t qrow0, int64_t krow0, int64_t i, int64_t lk, int64_t h, int64_t hk,
+                      int64_t heads, int64_t heads_kv, int64_t d, double scale, int causal,
+                      double *p, double *dp, double *lse_out) {
+  const double *qi = q + at(qrow0 + i, h, 0, heads, d);
+  const double *doi = dout + at(qrow0 + i, h, 0, heads, d);
+  double m = -INFINITY;
+  for (int64_t j = 0; j < lk; ++j) {
+    double acc = 0.0;
+    for (int64_t t = 0; t < d; ++t) acc += qi[t] * k[at(krow0 + j, hk, t, heads_kv, d)];
+    p[j] = (causal && j > i) ? -INFINITY : scale * acc;
+    if (p[j] > m) m = p[j];
+  }
+  double l = 0.0;
+  for (int64_t j = 0; j < lk; ++j) l += exp(p[j] - m);
+  for (int64_t j = 0; j < lk; ++j) p[j] = exp(p[j] - m) / l;
+  double di = 0.0;
+  for (int64_t j = 0; j < lk; ++j) {
+    double acc = 0.0;
+    for (int64_t t = 0; t < d; ++t) acc += doi[t] * v[at(krow0 + j, hk, t, heads_kv, d)];
+    dp[j] = acc;
+    di += p[j] * acc;
+  }
+  *lse_out = m + log(l);
+  return di;
+}
+
+/*
+ * Selected rows of the backward pass (for sampled checks at full size), the same definition
+ * as oracle_attention_bwd:
+ *  - qrows: n_qrows triples (b, h, i); dq_rows [n_qrows, d] receives dQ of query row i of head h;
+ *  - krows: n_krows triples (b, hk, j); dk_rows, dv_rows [n_krows, d] receive dK, dV of key j of
+ *    K/V head hk (summed over the query heads of its group).  For a key row every query row of
+ *    the group's heads contributes P_ij and dS_ij, which need that row's LSE and D; those are
+ *    computed for all rows of (b, hk) once, when the key rows move to a new (b, hk), so key rows
+ *    should be grouped by (b, hk).
+ * Layouts and cu as in oracle_attention.  Returns 0, -1 if memory could not be obtained, -2 if
+ * heads_kv does not divide heads.
+ */
+int oracle_attention_bwd_rows(const double *q, const double *k, const double *v, const double *dout,
+                              int64_t batch, int64_t nq, int64_t nk, int64_t heads, int64_t heads_kv,
+                              int64_t d, double scale, int causal, const int64_t *cu,
+                              const int64_t *qrows, int64_t n_qrows, double *dq_rows,
+                              const int64_t *krows, int64_t n_krows, double *dk_rows, double *dv_rows) {
+  if (heads_kv <= 0 || heads % heads_kv != 0) return -2;
+  const int64_t group = heads / heads_kv;
+  int64_t max_nk = nk, max_nq = nq;
+  if (cu) {
+    max_nk = 0;
+    for (int64_t b = 0; b < batch; ++b) if (cu[b + 1] - cu[b] > max_nk) max_nk = cu[b + 1] - cu[b];
+    max_nq = max_nk;
+  }
+  int failed = 0;
+  /* dQ rows: one query row each */
+#pragma omp parallel
+  {
+    double *p = (double *)malloc(sizeof(double) * (size_t)(max_nk > 0 ? max_nk : 1));
+    double *dp = (double *)malloc(sizeof(double) * (size_t)(max_nk > 0 ? max_nk : 1));
+    if (!p || !dp) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_qrows; ++r) {
+      if (!p || !dp) continue;
+      int64_t b = qrows[3 * r], h = qrows[3 * r + 1], i = qrows[3 * r + 2];
+      int64_t lk = cu ? cu[b + 1] - cu[b] : nk;
+      int64_t qrow0 = cu ? cu[b] : b * nq;
+      int64_t krow0 = cu ? cu[b] : b * nk;
+      double lse;
+      double di = bwd_row(q, k, v, dout, qrow0, krow0, i, lk, h, h / group, heads, heads_kv, d, scale,
+                          causal, p, dp, &lse);
+      for (int64_t t = 0; t < d; ++t) dq_rows[r * d + t] = 0.0;
+      for (int64_t j = 0; j < lk; ++j) {
+        double ds = p[j] * (dp[j] - di);
+        for (int64_t t = 0; t < d; ++t) dq_rows[r * d + t] += scale * ds * k[at(krow0 + j, h / group, t, heads_kv, d)];
+      }
+    }
+    free(p);
+    free(dp);
+  }
+  if (failed) return -1;
+  /* dK, dV rows: LSE and D of every query row of the group, then the sums over query rows */
+  double *lse_all = (double *)malloc(sizeof(double) * (size_t)(group * (max_nq > 0 ? max_nq : 1)));
+  double *d_all = (double *)malloc(sizeof(double) * (size_t)(group * (max_nq > 0 ? max_nq : 1)));
+  if (!lse_all || !d_all) {
+    free(lse_all);
+    free(d_all);
+    return -1;
+  }
+  int64_t cur_b = -1, cur_hk = -1;
+  for (int64_t r = 0; r < n_krows && !failed; ++r) {
+    int64_t b = krows[3 * r], hk = krows[3 * r + 1], j = krows[3 * r + 2];
+    int64_t lq = cu ? cu[b + 1] - cu[b] : nq;
+    int64_t lk = cu ? cu[b + 1] - cu[b] : nk;
+    int64_t qrow0 = cu ? cu[b] : b * nq;
+    int64_t krow0 = cu ? cu[b] : b * nk;
+    if (b != cur_b || hk != cur_hk) {
+#pragma omp parallel
+      {
+        double *p = (double *)malloc(sizeof(double) * (size_t)(max_nk > 0 ? max_nk : 1));
+        double *dp = (double *)malloc(sizeof(double) * (size_t)(max_nk > 0 ? max_nk : 1));
+        if (!p || !dp) {
+#pragma omp atomic write
+          failed = 1;
+        }
+#pragma omp for collapse(2) schedule(dynamic, 4)
+        for (int64_t g = 0; g < group; ++g)
+          for (int64_t i = 0; i < lq; ++i) {
+            if (!p || !dp) continue;
+            double lse;
+            d_all[g * max_nq + i] = bwd_row(q, k, v, dout, qrow0, krow0, i, lk, hk * group + g, hk, heads,
+                                            heads_kv, d, scale, causal, p, dp, &lse);
+            lse_all[g * max_nq + i] = lse;
+          }
+        free(p);
+        free(dp);
+      }
+      cur_b = b;
+      cur_hk = hk;
+      if (failed) break;
+    }
+    for (int64_t t = 0; t < d; ++t) {
+      dk_rows[r * d + t] = 0.0;
+      dv_rows[r * d + t] = 0.0;
+    }
+    for (int64_t g = 0; g < group; ++g) {
+      int64_t h = hk * group + g;
+      for (int64_t i = 0; i < lq; ++i) {
+        if (causal && j > i) continue; /* P_ij = 0 */
+        const double *qi = q + at(qrow0 + i, h, 0, heads, d);
+        const double *doi = dout + at(qrow0 + i, h, 0, heads, d);
+        double s = 0.0, dpij = 0.0;
+        for (int64_t t = 0; t < d; ++t) {
+          s += qi[t] * k[at(krow0 + j, hk, t, heads_kv, d)];
+          dpij += doi[t] * v[at(krow0 + j, hk, t, heads_kv, d)];
+        }
+        double pij = exp(scale * s - lse_all[g * max_nq + i]);
+        double ds = pij * (dpij - d_all[g * max_nq + i]);
+        for (int64_t t = 0; t < d; ++t) {
+          dv_rows[r * d + t] += pij * doi[t];
+          dk_rows[r * d + t] += scale * ds * qi[t];
+        }
+      }
+    }
+  }
+  free(lse_all);
+  free(d_all);
+  return failed ? -1 : 0;
+}
+
 /* Number of OpenMP threads the oracle runs with (for reporting). */
 int oracle_num_threads(void) {
   int n = 1;

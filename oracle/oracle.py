@@ -58,6 +58,10 @@ def _bind(path):
     lib.oracle_attention_bwd.restype = ctypes.c_int
     lib.oracle_attention_bwd.argtypes = [_D, _D, _D, _D, _D, _D, _D, _i64, _i64, _i64, _i64, _i64, _i64,
                                          ctypes.c_double, ctypes.c_int, _I64]
+    lib.oracle_attention_bwd_rows.restype = ctypes.c_int
+    lib.oracle_attention_bwd_rows.argtypes = [_D, _D, _D, _D, _i64, _i64, _i64, _i64, _i64, _i64,
+                                              ctypes.c_double, ctypes.c_int, _I64, _I64, _i64, _D, _I64, _i64,
+                                              _D, _D]
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
 
@@ -198,6 +202,41 @@ def attention_bwd(q, k, v, dout, scale, cu_seqlens=None, max_seqlen=None, causal
     return dq, dk, dv
 
 
+def attention_bwd_rows(q, k, v, dout, scale, qrows=(), krows=(), cu_seqlens=None, max_seqlen=None,
+                       causal=False, _lib_override=None):
+    """Selected rows of the backward pass in fp64: dQ of query rows (b, h, i) and dK, dV of key
+    rows (b, hk, j).  Returns (dQ [n_q, D], dK [n_k, D], dV [n_k, D]).  Key rows are best
+    grouped by (b, hk): the per-row LSE and D of a (b, hk) are computed once per group."""
+    lib = _lib_override or _load()
+    batch, nq, nk, heads, hkv, d, cu = _shapes(np.asarray(q), np.asarray(k), np.asarray(v),
+                                               cu_seqlens, max_seqlen)
+    qr = np.ascontiguousarray(np.asarray(qrows, dtype=np.int64).reshape(-1, 3))
+    kr = np.ascontiguousarray(np.asarray(krows, dtype=np.int64).reshape(-1, 3))
+    for b, h, i in qr:
+        lq = (cu[b + 1] - cu[b]) if cu is not None else nq
+        if not (0 <= b < batch and 0 <= h < heads and 0 <= i < lq):
+            raise IndexError("query row (%d, %d, %d) out of range" % (b, h, i))
+    for b, hk, j in kr:
+        lk = (cu[b + 1] - cu[b]) if cu is not None else nk
+        if not (0 <= b < batch and 0 <= hk < hkv and 0 <= j < lk):
+            raise IndexError("key row (%d, %d, %d) out of range" % (b, hk, j))
+    q, qp = _f64(q)
+    k, kp = _f64(k)
+    v, vp = _f64(v)
+    dout, dop = _f64(dout)
+    dq = np.zeros((qr.shape[0], d), dtype=np.float64)
+    dk = np.zeros((kr.shape[0], d), dtype=np.float64)
+    dv = np.zeros((kr.shape[0], d), dtype=np.float64)
+    cup = cu.ctypes.data_as(_I64) if cu is not None else None
+    rc = lib.oracle_attention_bwd_rows(qp, kp, vp, dop, batch, nq, nk, heads, hkv, d, float(scale),
+                                       int(bool(causal)), cup, qr.ctypes.data_as(_I64), qr.shape[0],
+                                       dq.ctypes.data_as(_D), kr.ctypes.data_as(_I64), kr.shape[0],
+                                       dk.ctypes.data_as(_D), dv.ctypes.data_as(_D))
+    if rc != 0:
+        raise MemoryError("oracle_attention_bwd_rows failed")
+    return dq, dk, dv
+
+
 def num_threads():
     """OpenMP threads the oracle runs with."""
     return int(_load().oracle_num_threads())
@@ -224,6 +263,9 @@ class Oracle:
 
     def attention_bwd(self, *a, **kw):
         return attention_bwd(*a, _lib_override=self._lib, **kw)
+
+    def attention_bwd_rows(self, *a, **kw):
+        return attention_bwd_rows(*a, _lib_override=self._lib, **kw)
 
 
 def compile_source(src_text, out_path):

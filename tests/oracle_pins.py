@@ -415,6 +415,35 @@ def pin_bwd_identical_keys_and_single_key(orc):
     np.testing.assert_allclose(dv1[:, 0], dout.sum(axis=1), rtol=0, atol=1e-12)
 
 
+def pin_bwd_rows_match_full(orc):
+    """The selected-rows backward returns the full backward's rows: dQ of query rows, dK and dV
+    of key rows, dense and packed, plain and causal, grouped heads."""
+    rng = np.random.default_rng(32)
+    q, dout = _rand(rng, 2, 9, 4, 8), _rand(rng, 2, 9, 4, 8)
+    k, v = _rand(rng, 2, 11, 2, 8), _rand(rng, 2, 11, 2, 8)
+    for causal in (False, True):
+        dq, dk, dv = orc.attention_bwd(q, k, v, dout, 0.5, causal=causal)
+        qrows = [(0, 0, 0), (1, 3, 8), (0, 2, 4), (1, 1, 3)]
+        krows = [(0, 0, 0), (0, 0, 10), (0, 1, 5), (1, 1, 2), (1, 0, 7)]
+        gq, gk, gv = orc.attention_bwd_rows(q, k, v, dout, 0.5, qrows, krows, causal=causal)
+        for n, (b, h, i) in enumerate(qrows):
+            np.testing.assert_allclose(gq[n], dq[b, i, h], rtol=0, atol=1e-13)
+        for n, (b, hk, j) in enumerate(krows):
+            np.testing.assert_allclose(gk[n], dk[b, j, hk], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(gv[n], dv[b, j, hk], rtol=0, atol=1e-13)
+    lens = [4, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    qp, dp = _rand(rng, 13, 2, 8), _rand(rng, 13, 2, 8)
+    kp, vp = _rand(rng, 13, 2, 8), _rand(rng, 13, 2, 8)
+    dq, dk, dv = orc.attention_bwd(qp, kp, vp, dp, 0.5, cu_seqlens=cu, causal=True)
+    gq, gk, gv = orc.attention_bwd_rows(qp, kp, vp, dp, 0.5, [(1, 1, 8), (0, 0, 3)], [(1, 0, 0), (1, 1, 8)],
+                                        cu_seqlens=cu, causal=True)
+    np.testing.assert_allclose(gq[0], dq[4 + 8, 1], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(gq[1], dq[3, 0], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(gk[0], dk[4, 0], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(gv[1], dv[4 + 8, 1], rtol=0, atol=1e-13)
+
+
 PINS = [pin_hand_2x2, pin_hand_4x4, pin_values_one, pin_identical_keys, pin_dominant_logit,
         pin_value_identity_is_softmax, pin_single_key, pin_permutations_and_linearity,
         pin_shift_invariance, pin_large_logits, pin_online_recurrence_is_exact,
@@ -422,4 +451,4 @@ PINS = [pin_hand_2x2, pin_hand_4x4, pin_values_one, pin_identical_keys, pin_domi
         pin_causal_identical_keys, pin_causal_value_identity, pin_causal_is_prefix_attention,
         pin_causal_block_skipping_is_exact, pin_causal_varlen_is_per_sequence,
         pin_grouped_heads_are_repeated_heads, pin_bwd_finite_differences, pin_bwd_tiny_all_coordinates,
-        pin_bwd_value_identities, pin_bwd_identical_keys_and_single_key]
+        pin_bwd_value_identities, pin_bwd_identical_keys_and_single_key, pin_bwd_rows_match_full]

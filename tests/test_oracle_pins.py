@@ -49,6 +49,9 @@ MUTATIONS = {
     "bwd_dp_uses_k": ("for (int64_t t = 0; t < d; ++t) acc += doi[t] * v[at(krow0 + j, hk, t, heads_kv, d)];",
                       "for (int64_t t = 0; t < d; ++t) acc += doi[t] * k[at(krow0 + j, hk, t, heads_kv, d)];"),
     "bwd_causal_ignored": ("p[j] = (causal && j > i) ? -INFINITY : scale * acc;", "p[j] = scale * acc;"),
+    "bwd_rows_dk_without_D": ("double ds = pij * (dpij - d_all[g * max_nq + i]);", "double ds = pij * dpij;"),
+    "bwd_rows_dq_wrong_head": ("dq_rows[r * d + t] += scale * ds * k[at(krow0 + j, h / group, t, heads_kv, d)];",
+                               "dq_rows[r * d + t] += scale * ds * k[at(krow0 + j, 0, t, heads_kv, d)];"),
     "bwd_group_first_head_only": ("for (int64_t h = hk * group; h < (hk + 1) * group; ++h)",
                                   "for (int64_t h = hk * group; h < hk * group + 1; ++h)"),
 }
