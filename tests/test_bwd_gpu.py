@@ -129,3 +129,63 @@ def test_bwd_separate_dq_pass_is_deterministic():
 def test_bwd_longer_sequence():
     check_dense(1, 1024, 1024, 2, 2, 128, "bf16", True, seed=71)
     check_dense(1, 1024, 1024, 2, 1, 128, "bf16", False, seed=72)
+
+
+# ------------------------------------------------------------------------------ full size
+def _sampled_rows(rng, n_rows, heads, n, extra):
+    return sorted(set([(int(rng.integers(heads)), int(rng.integers(n_rows))) for _ in range(n)] + extra))
+
+
+@pytest.mark.parametrize("name", ["full", "causal", "gqa", "varlen"])
+def test_bwd_full_size_sampled_rows(name):
+    """The named workload at full size, as the benchmark runs it: dQ on sampled query rows and
+    dK, dV on sampled key rows of two sequences, against the oracle's selected-rows backward."""
+    w = inputs.workload(name)
+    dev = torch.device("cuda:0")
+    say("case bwd full size %s" % name)
+    qd, kd, vd = w["q"].to(dev), w["k"].to(dev), w["v"].to(dev)
+    cu = w["cu_seqlens"]
+    cud = cu.to(dev) if cu is not None else None
+    o, lse = fa.fa_fwd_ext(qd, kd, vd, scale=w["scale"], causal=w["causal"], cu_seqlens=cud,
+                           max_seqlen=w["max_seqlen"])
+    do = dout_like(w["q"], w["seed"] + 1000)
+    dq, dk, dv = fa.fa_bwd(qd, kd, vd, o, lse, do.to(dev), scale=w["scale"], causal=w["causal"], cu_seqlens=cud,
+                           max_seqlen=w["max_seqlen"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(len(name) + 7)
+    heads, hkv = w["heads"], w["heads_kv"]
+    errs = {"dQ": [], "dK": [], "dV": []}
+    refs = {"dQ": [], "dK": [], "dV": []}
+    seqs = [0, w["batch"] - 1]
+    for b in seqs:
+        if cu is None:
+            sl = (slice(b, b + 1),)
+            n = w["seqlen_q"]
+            take = lambda t: t[b]  # noqa: E731
+        else:
+            s0, s1 = int(cu[b]), int(cu[b + 1])
+            n = s1 - s0
+            take = lambda t, s0=s0, s1=s1: t[s0:s1]  # noqa: E731
+        qrows = _sampled_rows(rng, n, heads, 24, [(0, 0), (heads - 1, n - 1)])
+        krows = sorted(set((hk, j) for hk in (0, hkv - 1)
+                           for j in [0, n - 1] + [int(x) for x in rng.integers(n, size=10)]))
+        if cu is None:
+            qb, kb, vb, db = (inputs.to_f64(t[b:b + 1]) for t in (w["q"], w["k"], w["v"], do))
+        else:
+            qb, kb, vb, db = (inputs.to_f64(take(t)[None]) for t in (w["q"], w["k"], w["v"], do))
+        rq, rk, rv = oracle.attention_bwd_rows(qb, kb, vb, db, w["scale"], [(0, h, i) for h, i in qrows],
+                                               [(0, hk, j) for hk, j in krows], causal=w["causal"])
+        gq = take(dq)[[i for _, i in qrows], [h for h, _ in qrows]].cpu().to(torch.float64).numpy()
+        gk = take(dk)[[j for _, j in krows], [hk for hk, _ in krows]].cpu().to(torch.float64).numpy()
+        gv = take(dv)[[j for _, j in krows], [hk for hk, _ in krows]].cpu().to(torch.float64).numpy()
+        for key, g, r in (("dQ", gq, rq), ("dK", gk, rk), ("dV", gv, rv)):
+            errs[key].append(np.abs(g - r).ravel())
+            refs[key].append(np.abs(r).ravel())
+    bad = []
+    for key in ("dQ", "dK", "dV"):
+        err, ref = np.concatenate(errs[key]), np.concatenate(refs[key])
+        say("%s %s (%d sampled values): max err %.3g (ref max %.3g)  mean err %.3g (ref mean %.3g)"
+            % (name, key, err.size, err.max(), ref.max(), err.mean(), ref.mean()))
+        if not (err.max() <= REL_MAX * ref.max() + ABS_MAX and err.mean() <= REL_MEAN * ref.mean() + ABS_MEAN):
+            bad.append(key)
+    assert not bad, (name, bad)
