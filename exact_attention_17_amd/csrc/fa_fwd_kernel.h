@@ -596,8 +596,9 @@ fa_fwd_kernel(FaArgs a) {
     constexpr int STAGE = 2 * TILE;  // K tile then V tile
     constexpr int LPT = 2 * (NCH >= NW ? NCH / NW : 1);  // loads per tile of a loading wavefront
     static_assert(NCH % NW == 0 || NW % NCH == 0, "tile pieces spread evenly");
-    auto step = [&](auto st_c, int j) __attribute__((always_inline)) {
+    auto step = [&](auto st_c, auto mask_c, int j) __attribute__((always_inline)) {
       constexpr int ST = decltype(st_c)::value;
+      constexpr bool MK = decltype(mask_c)::value;
       if constexpr (STAGES == 1) {
         if (j > 0) {
           __syncthreads();  // everyone is done with tile j-1
@@ -623,14 +624,30 @@ fa_fwd_kernel(FaArgs a) {
           load_one(rv, smem + NS * STAGE + TILE, jb + j + STAGES - 1);
         }
       }
-      if ((jb + j) * BC < wave_kend) {  // else every key of the tile is masked for this wavefront
+      // (an unmasked tile has a key visible to every row of the wavefront; a masked one may
+      // have none, and is then skipped)
+      if (!MK || (jb + j) * BC < wave_kend) {
         f32x16 S[KB];
         i32x4 P[KS];
         bool rs;
         qk_block<D, BC, F16>(smem + ST * STAGE, S, qreg[0], ad);
-        const float alpha = softmax(S, P, 0, jb + j, rs);
+        const float alpha =
+            softmax_block<BC, F16, MK>(S, P, m[0], l[0], c, MK ? klim[0] - (jb + j) * BC - 4 * hi : 0, rs);
         if (rs) rescale_o<DT>(O[0], alpha);
         pv_block<D, BC, F16>(smem + ST * STAGE + TILE, P, O[0], ad);
+      }
+    };
+    // Tiles [0, jm) hold no masked key for this wavefront, tiles [jm, ntl) may.  Each range
+    // runs in a loop of its own: with one loop and a branch around the masking, the scores
+    // (or, with the branch around the whole tile, the output accumulators) of the two paths
+    // meet at the end of every step and the compiler copies all of them between registers.
+    const int jm = min(max(kfull[0] - jb, 0), ntl);
+    auto run = [&](auto mask_c, int j0, int j1) __attribute__((always_inline)) {
+      for (int jj = j0 - j0 % STAGES; jj < j1; jj += STAGES) {
+        static_for<0, STAGES>([&](auto st_c) __attribute__((always_inline)) {
+          const int j = jj + decltype(st_c)::value;
+          if (j >= j0 && j < j1) step(st_c, mask_c, j);
+        });
       }
     };
 #pragma unroll
@@ -640,11 +657,8 @@ fa_fwd_kernel(FaArgs a) {
         load_one(rv, smem + t * STAGE + TILE, jb + t);
       }
     }
-    for (int j = 0; j < ntl; j += STAGES) {
-      static_for<0, STAGES>([&](auto st_c) __attribute__((always_inline)) {
-        if (j + decltype(st_c)::value < ntl) step(st_c, j + decltype(st_c)::value);
-      });
-    }
+    run(std::false_type{}, 0, jm);
+    run(std::true_type{}, jm, ntl);
     finish(0);
   } else if constexpr (SCHED == 1) {
     // Dual-block software pipeline (see the header comment).  Step j:
