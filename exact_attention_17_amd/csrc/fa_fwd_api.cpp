@@ -90,7 +90,13 @@ int log2_bucket(int n) {
 // otherwise two workgroups of four.
 fa_tile_config_t default_config(int seqlen_q, int d, bool causal) {
   if (seqlen_q <= 64) return fa_tile_config_t{64, 64, 2, 2, 0};
-  if (d == 128 && seqlen_q > 128 && !causal) return fa_tile_config_t{256, 64, 8, 2, 0};
+  if (d == 128 && seqlen_q > 128) {
+    // Under the causal mask half the key tiles are skipped and the diagonal ones are short;
+    // three four-wavefront workgroups per CU (32-key tiles) then hide more of each step's
+    // latency than the eight-wavefront tile does (about 7% on B16 N4096 H16).
+    if (causal) return fa_tile_config_t{128, 32, 4, 2, 4};
+    return fa_tile_config_t{256, 64, 8, 2, 0};
+  }
   return fa_tile_config_t{128, 64, 4, 2, 0};
 }
 
@@ -424,6 +430,15 @@ int fa_fwd_get_config(int batch, int seqlen_q, int seqlen_k, int n_heads, int d_
     return fail(FA_ERR_INVALID_ARG, "batch, n_heads, seqlen_q and seqlen_k must be >= 1");
   if (!valid_d(d_head)) return fail(FA_ERR_UNSUPPORTED, "d_head must be 32, 64 or 128");
   *out = choose_config(seqlen_q, d_head, dtype, varlen != 0, false);
+  return ok();
+}
+
+int fa_fwd_get_config_ext(int batch, int seqlen_q, int seqlen_k, int n_heads, int d_head, int dtype,
+                          int varlen, int causal, fa_tile_config_t *out) {
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  const int st = fa_fwd_get_config(batch, seqlen_q, seqlen_k, n_heads, d_head, dtype, varlen, out);
+  if (st != FA_OK) return st;
+  *out = choose_config(seqlen_q, d_head, dtype, varlen != 0, causal != 0);
   return ok();
 }
 

@@ -20,6 +20,8 @@ void register_bf16_d32(void (*add)(const KernelEntry &)) {
   add(make_entry<32, 256, 64, 8, 4, false>());
   add(make_entry<32, 256, 32, 8, 4, false>());
   add(make_entry<32, 128, 32, 4, 3, false>());
+  add(make_entry<32, 128, 32, 4, 2, false, 4>());
+  add(make_entry<32, 128, 32, 4, 3, false, 4>());
 }
 
 }  // namespace fa

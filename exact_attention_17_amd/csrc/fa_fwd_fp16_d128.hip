@@ -20,6 +20,8 @@ void register_fp16_d128(void (*add)(const KernelEntry &)) {
   add(make_entry<128, 256, 64, 8, 4, true>());
   add(make_entry<128, 256, 32, 8, 4, true>());
   add(make_entry<128, 128, 32, 4, 3, true>());
+  add(make_entry<128, 128, 32, 4, 2, true, 4>());
+  add(make_entry<128, 128, 32, 4, 3, true, 4>());
 }
 
 }  // namespace fa

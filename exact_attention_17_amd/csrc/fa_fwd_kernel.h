@@ -36,9 +36,15 @@
 //    run on the same XCD and share its L2 for K/V; an XCD's range runs over
 //    heads first, so every XCD gets a share of every (packed) sequence.
 //
-// Three schedules:
+// Schedules:
 //  SCHED 0: each wavefront owns one 32-row block and runs QK^T, softmax and
 //    PV of a tile in turn (two wavefronts per SIMD hide each other's stalls).
+//    Tiles with no masked key and the others run in separate loops.
+//  SCHED 4: SCHED 0 with 32-key tiles at three wavefronts per SIMD (three
+//    independent four-wavefront workgroups per CU).  A wavefront's step is a
+//    chain of latencies (LDS reads, the matrix results, the row max, the
+//    barrier) about twice as long as its own matrix work; a third wavefront
+//    per SIMD hides more of it than the shorter tiles cost.
 //  SCHED 1: each wavefront owns two 32-row blocks A and B (one wavefront per
 //    SIMD, 512 registers) and software-pipelines them so that the softmax of
 //    one block (vector ALU) is issued between the matrix instructions of the
@@ -223,10 +229,13 @@ using IC = std::integral_constant<int, V>;
 
 // S^T = K_tile Q^T for one 32-query block: KB accumulators of 32 keys x 32 queries.  MFMA i
 // (t = i / KB, kb = i % KB) reads its K operand LA reads ahead.
-template <int D, int BC, bool F16, int LA = 6>
+// SOFF is a byte offset from sk carried in the reads' immediate field, so that the per-lane
+// addresses (one register per d step) do not depend on which ring slot is read.
+template <int D, int BC, bool F16, int LA = 6, int SOFF = 0>
 __device__ __forceinline__ void qk_block(const char *sk, f32x16 (&S)[BC / 32], const i32x4 (&qr)[D / 16],
                                          const LdsAddr &ad) {
   constexpr int ROWB = D * 2, KB = BC / 32, T = D / 16, N = T * KB;
+  static_assert(SOFF + (KB - 1) * 32 * ROWB < 65536, "ds_read offset field");
   constexpr int L = LA < N ? LA : N;
   const uint32_t sk_lds = (uint32_t)(uintptr_t)(const char FA_LDS *)sk;
   uint32_t koff[T];
@@ -237,7 +246,7 @@ __device__ __forceinline__ void qk_block(const char *sk, f32x16 (&S)[BC / 32], c
   i32x4 buf[L + 1];
   auto issue = [&buf, &koff](auto i_c) __attribute__((always_inline)) {
     constexpr int i = decltype(i_c)::value;
-    lds_read_b128<(i % KB) * 32 * ROWB>(buf[i % (L + 1)], koff[i / KB]);
+    lds_read_b128<SOFF + (i % KB) * 32 * ROWB>(buf[i % (L + 1)], koff[i / KB]);
   };
   static_for<0, L>(issue);
   static_for<0, N>([&](auto i_c) __attribute__((always_inline)) {
@@ -254,11 +263,13 @@ __device__ __forceinline__ void qk_block(const char *sk, f32x16 (&S)[BC / 32], c
 // 16 ks + 4(l/32) + {0..3} and 16 ks + 8 + 4(l/32) + {0..3}: two transposed reads, each fed
 // by lanes that point at four rows x 4 consecutive d of the row-major V tile.  MFMA i
 // (ks = i / DT, dt = i % DT) has its two reads issued LA MFMAs ahead.
-template <int D, int BC, bool F16, int LA = 4>
+// (SOFF as in qk_block)
+template <int D, int BC, bool F16, int LA = 4, int SOFF = 0>
 __device__ __forceinline__ void pv_block(const char *sv, const i32x4 (&P)[BC / 16], f32x16 (&O)[D / 32],
                                          const LdsAddr &ad) {
   constexpr int ROWB = D * 2, DT = D / 32, KS = BC / 16, N = KS * DT;
   constexpr int L = LA < N ? LA : N;
+  static_assert(SOFF + 16 * (KS - 1) * ROWB < 65536, "ds_read offset field");
   static_assert(2 * L <= 15, "lgkmcnt field");
   const uint32_t sv_lds = (uint32_t)(uintptr_t)(const char FA_LDS *)sv;
   uint32_t a0[DT], a1[DT];
@@ -270,8 +281,8 @@ __device__ __forceinline__ void pv_block(const char *sv, const i32x4 (&P)[BC / 1
   i16x4 b0[L + 1], b1[L + 1];
   auto issue = [&b0, &b1, &a0, &a1](auto i_c) __attribute__((always_inline)) {
     constexpr int i = decltype(i_c)::value;
-    lds_read_tr<16 * (i / DT) * ROWB>(b0[i % (L + 1)], a0[i % DT]);
-    lds_read_tr<16 * (i / DT) * ROWB>(b1[i % (L + 1)], a1[i % DT]);
+    lds_read_tr<SOFF + 16 * (i / DT) * ROWB>(b0[i % (L + 1)], a0[i % DT]);
+    lds_read_tr<SOFF + 16 * (i / DT) * ROWB>(b1[i % (L + 1)], a1[i % DT]);
   };
   static_for<0, L>(issue);
   static_for<0, N>([&](auto i_c) __attribute__((always_inline)) {
@@ -416,7 +427,7 @@ __device__ __forceinline__ void store_block_part(const f32x16 (&O)[D / 32], floa
 
 template <int SCHED>
 constexpr int waves_per_simd() {
-  return SCHED == 1 ? 1 : 2;
+  return SCHED == 1 ? 1 : SCHED == 4 ? 3 : 2;
 }
 
 // Workgroup barrier without the memory fences of __syncthreads (which would also wait for
@@ -445,7 +456,8 @@ fa_fwd_kernel(FaArgs a) {
   static_assert(D == 32 || D == 64 || D == 128, "d_head");
   static_assert(BC % 32 == 0 && TILE % 1024 == 0, "tile shape");
   static_assert(STAGES >= 1 && STAGES <= 4, "stages");
-  static_assert(SCHED == 0 || (SCHED == 1 && STAGES == 2) || (SCHED == 2 && STAGES == 2 && NW == 8),
+  static_assert(SCHED == 0 || (SCHED == 1 && STAGES == 2) || (SCHED == 2 && STAGES == 2 && NW == 8) ||
+                    (SCHED == 4 && BC == 32),
                 "schedule");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
@@ -589,7 +601,10 @@ fa_fwd_kernel(FaArgs a) {
       store_block<D, F16>(O[nb], m[nb], l[nb], c, wrow0 + 32 * nb, nq, row_bytes, ro, lse_row, lane);
   };
 
-  if constexpr (SCHED == 0) {
+  if constexpr (SCHED == 0 || SCHED == 4) {
+    // (schedule 4 is this loop at three wavefronts per SIMD: 32-key tiles and shorter LDS
+    // read lookahead keep a lane within 168 registers)
+    constexpr int QK_LA = SCHED == 4 ? 3 : 6, PV_LA = SCHED == 4 ? 2 : 4;
     // STAGES (K, V) tile pairs in LDS, tile j in stage j % STAGES; tile j + STAGES - 1 is
     // requested at the start of step j (its stage held tile j - 1, which every wavefront
     // finished before the barrier that opens step j), so STAGES - 1 tiles are in flight.
@@ -630,11 +645,15 @@ fa_fwd_kernel(FaArgs a) {
         f32x16 S[KB];
         i32x4 P[KS];
         bool rs;
-        qk_block<D, BC, F16>(smem + ST * STAGE, S, qreg[0], ad);
+        // the slot's offset goes into the reads' immediate field when it fits
+        constexpr int SO = ST * STAGE;
+        constexpr bool IMM = SO + STAGE <= 65536;
+        const char *base = IMM ? smem : smem + SO;
+        qk_block<D, BC, F16, QK_LA, IMM ? SO : 0>(base, S, qreg[0], ad);
         const float alpha =
             softmax_block<BC, F16, MK>(S, P, m[0], l[0], c, MK ? klim[0] - (jb + j) * BC - 4 * hi : 0, rs);
         if (rs) rescale_o<DT>(O[0], alpha);
-        pv_block<D, BC, F16>(smem + ST * STAGE + TILE, P, O[0], ad);
+        pv_block<D, BC, F16, PV_LA, (IMM ? SO : 0) + TILE>(base, P, O[0], ad);
       }
     };
     // Tiles [0, jm) hold no masked key for this wavefront, tiles [jm, ntl) may.  Each range
@@ -727,22 +746,33 @@ fa_fwd_kernel(FaArgs a) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     wg_barrier();
     if (grp == 1) wg_barrier();
-    for (int j = 0; j <= ntl; ++j) {
-      if (grp == 0) {
-        if (j + 1 < ntl) load_by(rk, kslot(j + 1), jb + j + 1, gw, Four{});
-        if (j < ntl) load_by(rv, vslot(j), jb + j, gw, Four{});
+    // One instance of the loop when no tile of the wavefront needs the mask (the usual case
+    // without the causal mask), so that the unmasked softmax is straight-line code; the
+    // other chooses per tile.
+    auto loop = [&](auto mask_c) __attribute__((always_inline)) {
+      constexpr bool ANY = decltype(mask_c)::value;
+      for (int j = 0; j <= ntl; ++j) {
+        if (grp == 0) {
+          if (j + 1 < ntl) load_by(rk, kslot(j + 1), jb + j + 1, gw, Four{});
+          if (j < ntl) load_by(rv, vslot(j), jb + j, gw, Four{});
+        }
+        if (j >= 1) pv_block<D, BC, F16>(vslot(j - 1), P, O[0], ad);
+        if (j < ntl) qk_block<D, BC, F16>(kslot(j), S, qreg[0], ad);
+        wg_barrier();
+        if (j < ntl) {
+          bool rs;
+          const float alpha =
+              ANY ? softmax(S, P, 0, jb + j, rs) : softmax_block<BC, F16, false>(S, P, m[0], l[0], c, 0, rs);
+          if (rs) rescale_o<DT>(O[0], alpha);
+        }
+        if (grp == 0) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        wg_barrier();
       }
-      if (j >= 1) pv_block<D, BC, F16>(vslot(j - 1), P, O[0], ad);
-      if (j < ntl) qk_block<D, BC, F16>(kslot(j), S, qreg[0], ad);
-      wg_barrier();
-      if (j < ntl) {
-        bool rs;
-        const float alpha = softmax(S, P, 0, jb + j, rs);
-        if (rs) rescale_o<DT>(O[0], alpha);
-      }
-      if (grp == 0) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      wg_barrier();
-    }
+    };
+    if (kfull[0] - jb >= ntl)
+      loop(std::false_type{});
+    else
+      loop(std::true_type{});
     if (grp == 0) wg_barrier();
     finish(0);
   }

@@ -17,7 +17,7 @@ FA_MAX_SPLITS = 128
 # Every exported symbol of include/fa_fwd.h.
 EXPORTS = ("fa_fwd", "fa_fwd_ext", "fa_fwd_workspace_bytes", "fa_fwd_choose_splits", "fa_bwd",
            "fa_bwd_workspace_bytes",
-           "fa_fwd_autotune", "fa_fwd_set_config", "fa_fwd_get_config", "fa_fwd_num_configs", "fa_fwd_list_configs", "fa_fwd_config_lds_bytes",
+           "fa_fwd_autotune", "fa_fwd_set_config", "fa_fwd_get_config", "fa_fwd_get_config_ext", "fa_fwd_num_configs", "fa_fwd_list_configs", "fa_fwd_config_lds_bytes",
            "fa_fwd_config_resources", "fa_last_error", "fa_version")
 
 
@@ -76,6 +76,8 @@ def lib():
         L.fa_fwd_set_config.argtypes = [_i, _i, ctypes.POINTER(TileConfig)]
         L.fa_fwd_get_config.restype = _i
         L.fa_fwd_get_config.argtypes = [_i, _i, _i, _i, _i, _i, _i, ctypes.POINTER(TileConfig)]
+        L.fa_fwd_get_config_ext.restype = _i
+        L.fa_fwd_get_config_ext.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i, ctypes.POINTER(TileConfig)]
         L.fa_fwd_num_configs.restype = _i
         L.fa_fwd_num_configs.argtypes = [_i, _i]
         L.fa_fwd_list_configs.restype = _i
@@ -305,6 +307,13 @@ def fa_fwd_get_config(batch, seqlen_q, seqlen_k, n_heads, d_head, dtype, varlen=
     c = TileConfig()
     _check(lib().fa_fwd_get_config(batch, seqlen_q, seqlen_k, n_heads, d_head, dtype, int(bool(varlen)),
                                    ctypes.byref(c)))
+    return c
+
+
+def fa_fwd_get_config_ext(batch, seqlen_q, seqlen_k, n_heads, d_head, dtype, varlen=False, causal=False):
+    c = TileConfig()
+    _check(lib().fa_fwd_get_config_ext(batch, seqlen_q, seqlen_k, n_heads, d_head, dtype, int(bool(varlen)),
+                                       int(bool(causal)), ctypes.byref(c)))
     return c
 
 

@@ -214,6 +214,11 @@ int fa_fwd_set_config(int d_head, int dtype, const fa_tile_config_t *cfg);
 int fa_fwd_get_config(int batch, int seqlen_q, int seqlen_k, int n_heads, int d_head, int dtype,
                       int varlen, fa_tile_config_t *out);
 
+/* As fa_fwd_get_config, for a call of fa_fwd_ext with this causal flag (0 or 1): the
+ * configuration fa_fwd_ext would use (host-only lookup). */
+int fa_fwd_get_config_ext(int batch, int seqlen_q, int seqlen_k, int n_heads, int d_head, int dtype,
+                          int varlen, int causal, fa_tile_config_t *out);
+
 /* Number of compiled configurations for (d_head, dtype); < 0 on bad args. */
 int fa_fwd_num_configs(int d_head, int dtype);
 

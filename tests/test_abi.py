@@ -87,7 +87,9 @@ def test_config_registry_host_only():
             assert len(cfgs) == fa.fa_fwd_num_configs(d, dtype) >= 1
             for c in cfgs:
                 assert c.stages in (1, 2, 3, 4)
-                assert c.schedule in (0, 1, 2)
+                assert c.schedule in (0, 1, 2, 4)
+                if c.schedule == 4:
+                    assert c.bc == 32
                 tile = c.bc * d * 2
                 if c.schedule == 1:
                     assert c.br == 64 * c.waves and c.stages == 2
@@ -119,6 +121,17 @@ def test_default_and_forced_config():
     finally:
         fa.fa_fwd_set_config(128, fa.FA_BF16, None)
     assert fa.fa_fwd_get_config(16, 4096, 4096, 16, 128, fa.FA_BF16).as_tuple() == (256, 64, 8, 2, 0)
+
+
+def test_causal_default_config():
+    # the causal default at d_head 128 is the three-per-SIMD schedule on 32-key tiles
+    c = fa.fa_fwd_get_config_ext(16, 4096, 4096, 16, 128, fa.FA_BF16, causal=True)
+    assert c.as_tuple() == (128, 32, 4, 2, 4)
+    assert fa.fa_fwd_get_config_ext(16, 4096, 4096, 16, 128, fa.FA_BF16).as_tuple() == \
+        fa.fa_fwd_get_config(16, 4096, 4096, 16, 128, fa.FA_BF16).as_tuple()
+    # causal must be 0 or 1
+    st = fa.lib().fa_fwd_get_config_ext(1, 64, 64, 1, 128, fa.FA_BF16, 0, 2, ctypes.byref(fa.TileConfig()))
+    assert st == fa.FA_ERR_INVALID_ARG
 
 
 def test_autotune_rejects_bad_args_on_host():

@@ -207,10 +207,11 @@ def test_repeat_launches_bitwise_identical():
 
 
 @pytest.mark.parametrize("ref,alt", [((256, 32, 8, 2, 0), (256, 32, 4, 2, 1)),
-                                     ((256, 64, 8, 2, 0), (256, 64, 8, 2, 2))])
+                                     ((256, 64, 8, 2, 0), (256, 64, 8, 2, 2)),
+                                     ((128, 32, 4, 2, 0), (128, 32, 4, 2, 4))])
 def test_schedules_match_in_order_bitwise_on_ragged_shapes(ref, alt):
-    # The dual-block and ping-pong schedules reorder work inside or across wavefronts, not the
-    # arithmetic of a row, so with the same key tile they give the same bits.
+    # The dual-block, ping-pong and three-per-SIMD schedules reorder work inside or across
+    # wavefronts, not the arithmetic of a row, so with the same key tile they give the same bits.
     for (nq, nk) in [(300, 1000), (257, 64), (1, 130), (256, 4095)]:
         q, k, v = inputs.dense_qkv(2, nq, nk, 3, 128, "bf16", seed=nq + nk)
         try:
