@@ -201,7 +201,10 @@ __device__ __forceinline__ void store_rows(const f32x16 (&A)[D / 32], float mul,
 // BKV = 32 * NW keys per workgroup, BQ = 64 query rows per step (two 32-row blocks).
 // ATOMIC_DQ: also form dQ = dS K here and add it into the fp32 accumulator with atomics (the
 // pages' Algorithm 2); otherwise dQ is left to fa_bwd_dq_pass_kernel.
-template <int D, int NW, bool F16, bool ATOMIC_DQ>
+// CAUSAL must equal a.causal.  Without the atomic dQ, keys past the sequence end need no mask:
+// each lane's products touch only its own key's dK and dV columns, and those rows are never
+// stored (the store goes through a resource bounded by the sequence).
+template <int D, int NW, bool F16, bool ATOMIC_DQ, bool CAUSAL>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ATOMIC_DQ ? 1 : 2)))
 fa_bwd_kernel(BwdArgs a) {
   constexpr int BKV = 32 * NW;
@@ -306,7 +309,7 @@ fa_bwd_kernel(BwdArgs a) {
 
   // Query tiles: all of them, or under the causal mask those holding a row >= k0.
   const int nqt = (nq + BQ - 1) / BQ;
-  const int qt0 = a.causal ? min(k0 / BQ, nqt) : 0;
+  const int qt0 = CAUSAL ? min(k0 / BQ, nqt) : 0;
   const int nqt_w = nqt - qt0;
   const int n_steps = nqt_w * a.group;  // (query head, query tile) pairs
 
@@ -337,7 +340,8 @@ fa_bwd_kernel(BwdArgs a) {
   constexpr int NATOM = ATOMIC_DQ ? TPW * 16 : 0;
   static_assert(NATOM + 2 * (NCHQ / NW) + 1 <= 63, "vmcnt field");
 
-  for (int s = 0; s < n_steps; ++s) {
+  // Step s = (query head, query tile) in stage s & 1.
+  auto step = [&](int s) __attribute__((always_inline)) {
     // Step s's loads (and, before them, the K tile and registers) have landed once at most
     // the previous step's atomics are still in flight.
     if (s == 0)
@@ -349,18 +353,18 @@ fa_bwd_kernel(BwdArgs a) {
 
     const int h = hk * a.group + s / nqt_w;
     const int q0 = (qt0 + s % nqt_w) * BQ;
-    const char *sq = sqd + (s & 1) * 2 * QT;
-    const char *sdo = sq + QT;
+    const char *sq = sqd + (s & 1) * 2 * QT;  // Q of this stage, dO after it
     const float *sl2 = (const float *)(svec + (s & 1) * 2 * VT);
     const float *sdv = sl2 + BQ;
 
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+    static_for<0, QB>([&](auto qb_c) __attribute__((always_inline)) {
+      constexpr int qb = decltype(qb_c)::value;
+      constexpr int QO = qb * 32 * ROWB;  // this 32-row block of Q (dO at + QT)
       f32x16 S[1], dP[1];
       // (shorter read lookahead than the forward's: two wavefronts per SIMD hide latency and
-      // the registers are needed for dK and dV)
-      qk_block<D, 32, F16, 3>(sq + qb * 32 * ROWB, S, kreg, ad);
-      qk_block<D, 32, F16, 3>(sdo + qb * 32 * ROWB, dP, vreg, ad);
+      // the registers are needed for dK and dV).  Order: S, P, dV += P^T dO, then dP, dS,
+      // so that S and the packed P are dead before dP is formed.
+      qk_block<D, 32, F16, 3, QO>(sq, S, kreg, ad);
       // rows of this lane: query q0 + 32 qb + 8 g + 4 hi + r; L log2(e) and D are read from
       // LDS four rows at a time, and P and dS packed to 16 bits as they are formed
       const int rb = 32 * qb + 4 * hi;
@@ -369,21 +373,27 @@ fa_bwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 l2 = *(const f32x4 *)(sl2 + rb + 8 * g);
-        const f32x4 dd = *(const f32x4 *)(sdv + rb + 8 * g);
-        float pv[4], dsv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int e = 4 * g + r;
           float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[0][e], c, -l2[r]));
-          // masked: key past the sequence, or (causal) key past the query
-          const bool masked = my_key >= nk || (a.causal && my_key > qrow_base + 8 * g + r);
-          p = masked ? 0.f : p;
-          pv[r] = p;
-          dsv[r] = p * (dP[0][e] - dd[r]);
+          // masked: (causal) key past the query; with the atomic dQ also a key past the
+          // sequence, whose zero K row would otherwise meet an unbounded P in dS K
+          if ((ATOMIC_DQ && my_key >= nk) || (CAUSAL && my_key > qrow_base + 8 * g + r)) p = 0.f;
+          S[0][e] = p;
         }
         // register e = 4g + r of step s2 = g / 2, dword (g % 2) * 2 + r / 2
-        Pp[g >> 1][2 * (g & 1)] = pack2<F16>(pv[0], pv[1]);
-        Pp[g >> 1][2 * (g & 1) + 1] = pack2<F16>(pv[2], pv[3]);
+        Pp[g >> 1][2 * (g & 1)] = pack2<F16>(S[0][4 * g], S[0][4 * g + 1]);
+        Pp[g >> 1][2 * (g & 1) + 1] = pack2<F16>(S[0][4 * g + 2], S[0][4 * g + 3]);
+      }
+      pv_block<D, 32, F16, 2, QO + QT>(sq, Pp, dVt, ad);
+      qk_block<D, 32, F16, 3, QO + QT>(sq, dP, vreg, ad);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 dd = *(const f32x4 *)(sdv + rb + 8 * g);
+        float dsv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dsv[r] = S[0][4 * g + r] * (dP[0][4 * g + r] - dd[r]);
         dSp[g >> 1][2 * (g & 1)] = pack2<F16>(dsv[0], dsv[1]);
         dSp[g >> 1][2 * (g & 1) + 1] = pack2<F16>(dsv[2], dsv[3]);
       }
@@ -398,9 +408,8 @@ fa_bwd_kernel(BwdArgs a) {
           *(int2 *)(sds + kr * DSROWB + chunk * 16 + (col & 7) * 2) = val;
         }
       }
-      pv_block<D, 32, F16, 2>(sdo + qb * 32 * ROWB, Pp, dVt, ad);
-      pv_block<D, 32, F16, 2>(sq + qb * 32 * ROWB, dSp, dKt, ad);
-    }
+      pv_block<D, 32, F16, 2, QO>(sq, dSp, dKt, ad);
+    });
     if constexpr (ATOMIC_DQ) {
     wait_lds_all();
     wg_barrier();  // dS^T complete
@@ -434,7 +443,8 @@ fa_bwd_kernel(BwdArgs a) {
                                                           base + (uint32_t)(8 * g + r) * (uint32_t)(hd * 4), 0, 0);
     }
     }  // ATOMIC_DQ
-  }
+  };
+  for (int s = 0; s < n_steps; ++s) step(s);
 
   // dK = scale dS^T Q and dV = P^T dO of this wavefront's 32 keys.
   const auto rdk = make_rsrc((char *)a.dk + (krow0 * hkd + (int64_t)hk * D) * 2, (uint32_t)(nk - 1) * kv_row_bytes + ROWB);
@@ -451,7 +461,7 @@ fa_bwd_kernel(BwdArgs a) {
 //     dQ^T += K^T dS^T              (K read transposed; dS registers as the B operand)
 // so dQ is summed over every key on chip and written once: no accumulator, no atomics,
 // the same bits on every run.  No running max or rescale: P is final given L.
-template <int D, int BC, int NW, bool F16>
+template <int D, int BC, int NW, bool F16, bool CAUSAL>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 fa_bwd_dq_pass_kernel(BwdArgs a) {
   constexpr int BR = 32 * NW;
@@ -477,7 +487,7 @@ fa_bwd_dq_pass_kernel(BwdArgs a) {
   const int per = G >> 3, rem = G & 7, xcd = w & 7;
   const int lin = xcd * per + min(xcd, rem) + (w >> 3);
   const int qi = lin % n_qtiles;
-  const int qt = a.causal ? n_qtiles - 1 - qi : qi;
+  const int qt = CAUSAL ? n_qtiles - 1 - qi : qi;
   const int hb = lin / n_qtiles;  // head-major, as in the forward
   const int b = hb % a.batch;
   const int h = hb / a.batch;
@@ -547,15 +557,18 @@ fa_bwd_dq_pass_kernel(BwdArgs a) {
   for (int dt = 0; dt < DT; ++dt) dQt[dt] = f32x16{};
   const float c = a.scale_log2;
   const LdsAddr ad = lds_addr<D>(lane);
-  const int kend = a.causal ? min(nk, q_tile0 + BR) : nk;
+  const int kend = CAUSAL ? min(nk, q_tile0 + BR) : nk;
   const int nkt = (kend + BC - 1) / BC;
-  // visible keys of this lane's row: below klim; tiles below kfull need no mask for the wavefront
-  const int klim = a.causal ? min(nk, my_row + 1) : nk;
-  const int kfull = (a.causal ? min(nk, wrow0 + 1) : nk) / BC;
-  const int wave_kend = a.causal ? min(nk, wrow0 + 32) : nk;
+  // visible keys of this lane's row: below klim; tiles below kfull need no mask for the
+  // wavefront.  (A key past the sequence end is masked too: its zero K row times an unbounded
+  // P, when the row's LSE is very negative, is not zero.)
+  const int klim = CAUSAL ? min(nk, my_row + 1) : nk;
+  const int kfull = (CAUSAL ? min(nk, wrow0 + 1) : nk) / BC;
+  const int wave_kend = CAUSAL ? min(nk, wrow0 + 32) : nk;
 
-  auto step = [&](auto st_c, int j) __attribute__((always_inline)) {
+  auto step = [&](auto st_c, auto mask_c, int j) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value;
+    constexpr bool MK = decltype(mask_c)::value;
     wait_vmcnt<0>();
     wg_barrier();
     if (j + 1 < nkt) {
@@ -563,12 +576,12 @@ fa_bwd_dq_pass_kernel(BwdArgs a) {
       load_one(rk, smem + NS * STAGE, j + 1);
       load_one(rv, smem + NS * STAGE + TILE, j + 1);
     }
-    if (j * BC < wave_kend) {
+    if (!MK || j * BC < wave_kend) {
       f32x16 S[KB], dP[KB];
-      qk_block<D, BC, F16>(smem + ST * STAGE, S, qreg, ad);
-      qk_block<D, BC, F16>(smem + ST * STAGE + TILE, dP, doreg, ad);
+      // the stage's offset rides in the reads' immediate field
+      qk_block<D, BC, F16, 6, ST * STAGE>(smem, S, qreg, ad);
+      qk_block<D, BC, F16, 6, ST * STAGE + TILE>(smem, dP, doreg, ad);
       // key of register r in block kb: j BC + 32 kb + 8 (r / 4) + 4 hi + r % 4
-      const bool need_mask = j >= kfull;
       i32x4 dSp[KS];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
@@ -576,7 +589,7 @@ fa_bwd_dq_pass_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], c, -l2));
-          if (need_mask && j * BC + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3) >= klim) p = 0.f;
+          if (MK && j * BC + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3) >= klim) p = 0.f;
           dsv[r] = p * (dP[kb][r] - dd);
         }
 #pragma unroll
@@ -584,17 +597,24 @@ fa_bwd_dq_pass_kernel(BwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) dSp[2 * kb + s2][e] = pack2<F16>(dsv[8 * s2 + 2 * e], dsv[8 * s2 + 2 * e + 1]);
       }
-      pv_block<D, BC, F16>(smem + ST * STAGE, dSp, dQt, ad);
+      pv_block<D, BC, F16, 4, ST * STAGE>(smem, dSp, dQt, ad);
     }
   };
   if (nkt > 0) {
     load_one(rk, smem, 0);
     load_one(rv, smem + TILE, 0);
   }
-  for (int j = 0; j < nkt; j += 2) {
-    step(IC<0>{}, j);
-    if (j + 1 < nkt) step(IC<1>{}, j + 1);
-  }
+  // Tiles [0, jm) need no mask and [jm, nkt) may: each range in a loop of its own (with the
+  // mask under a branch the compiler copies the scores between registers on every tile).
+  const int jm = min(kfull, nkt);
+  auto run = [&](auto mask_c, int j0, int j1) __attribute__((always_inline)) {
+    for (int jj = j0 - (j0 & 1); jj < j1; jj += 2) {
+      if (jj >= j0) step(IC<0>{}, mask_c, jj);
+      if (jj + 1 < j1) step(IC<1>{}, mask_c, jj + 1);
+    }
+  };
+  run(std::false_type{}, 0, jm);
+  run(std::true_type{}, jm, nkt);
   (void)LPT;
   store_rows<D, F16>(dQt, a.scale, wrow0, row_bytes, rdq, lane);
 }
@@ -609,8 +629,9 @@ hipError_t launch_fa_bwd(const BwdArgs &a, hipStream_t stream) {
   hipError_t e = hipLaunchKernel((const void *)&fa_bwd_pre_kernel<D, F16>,
                                  dim3(bh * ((a.seqlen_q + RPB_PRE - 1) / RPB_PRE)), dim3(256), args, 0, stream);
   if (e != hipSuccess) return e;
-  e = hipLaunchKernel((const void *)&fa_bwd_kernel<D, NW, F16, ATOMIC_DQ>, dim3(a.total_wgs), dim3(NW * 64), args, 0,
-                      stream);
+  e = hipLaunchKernel(a.causal ? (const void *)&fa_bwd_kernel<D, NW, F16, ATOMIC_DQ, true>
+                               : (const void *)&fa_bwd_kernel<D, NW, F16, ATOMIC_DQ, false>,
+                      dim3(a.total_wgs), dim3(NW * 64), args, 0, stream);
   if (e != hipSuccess) return e;
   if constexpr (ATOMIC_DQ) {
     return hipLaunchKernel((const void *)&fa_bwd_dq_kernel<D, F16>, dim3(bh * ((a.seqlen_q + RPB_DQ - 1) / RPB_DQ)),
@@ -621,7 +642,8 @@ hipError_t launch_fa_bwd(const BwdArgs &a, hipStream_t stream) {
     constexpr int NWQ = D == 128 ? 8 : 4;
     constexpr int BCQ = D == 128 ? 32 : 64;
     constexpr int BRQ = 32 * NWQ;
-    return hipLaunchKernel((const void *)&fa_bwd_dq_pass_kernel<D, BCQ, NWQ, F16>,
+    return hipLaunchKernel(a.causal ? (const void *)&fa_bwd_dq_pass_kernel<D, BCQ, NWQ, F16, true>
+                                    : (const void *)&fa_bwd_dq_pass_kernel<D, BCQ, NWQ, F16, false>,
                            dim3(bh * ((a.seqlen_q + BRQ - 1) / BRQ)), dim3(NWQ * 64), args, 0, stream);
   }
 }
