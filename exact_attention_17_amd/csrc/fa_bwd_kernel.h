@@ -362,9 +362,10 @@ fa_bwd_kernel(BwdArgs a) {
       constexpr int QO = qb * 32 * ROWB;  // this 32-row block of Q (dO at + QT)
       f32x16 S[1], dP[1];
       // (shorter read lookahead than the forward's: two wavefronts per SIMD hide latency and
-      // the registers are needed for dK and dV).  Order: S, P, dV += P^T dO, then dP, dS,
-      // so that S and the packed P are dead before dP is formed.
+      // the registers are needed for dK and dV; S and dP back to back, then P and dS, then
+      // the two accumulating products: more independent work than forming dP after dV)
       qk_block<D, 32, F16, 3, QO>(sq, S, kreg, ad);
+      qk_block<D, 32, F16, 3, QO + QT>(sq, dP, vreg, ad);
       // rows of this lane: query q0 + 32 qb + 8 g + 4 hi + r; L log2(e) and D are read from
       // LDS four rows at a time, and P and dS packed to 16 bits as they are formed
       const int rb = 32 * qb + 4 * hi;
@@ -373,6 +374,8 @@ fa_bwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 l2 = *(const f32x4 *)(sl2 + rb + 8 * g);
+        const f32x4 dd = *(const f32x4 *)(sdv + rb + 8 * g);
+        float pv[4], dsv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int e = 4 * g + r;
@@ -380,23 +383,16 @@ fa_bwd_kernel(BwdArgs a) {
           // masked: (causal) key past the query; with the atomic dQ also a key past the
           // sequence, whose zero K row would otherwise meet an unbounded P in dS K
           if ((ATOMIC_DQ && my_key >= nk) || (CAUSAL && my_key > qrow_base + 8 * g + r)) p = 0.f;
-          S[0][e] = p;
+          pv[r] = p;
+          dsv[r] = p * (dP[0][e] - dd[r]);
         }
         // register e = 4g + r of step s2 = g / 2, dword (g % 2) * 2 + r / 2
-        Pp[g >> 1][2 * (g & 1)] = pack2<F16>(S[0][4 * g], S[0][4 * g + 1]);
-        Pp[g >> 1][2 * (g & 1) + 1] = pack2<F16>(S[0][4 * g + 2], S[0][4 * g + 3]);
-      }
-      pv_block<D, 32, F16, 2, QO + QT>(sq, Pp, dVt, ad);
-      qk_block<D, 32, F16, 3, QO + QT>(sq, dP, vreg, ad);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 dd = *(const f32x4 *)(sdv + rb + 8 * g);
-        float dsv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dsv[r] = S[0][4 * g + r] * (dP[0][4 * g + r] - dd[r]);
+        Pp[g >> 1][2 * (g & 1)] = pack2<F16>(pv[0], pv[1]);
+        Pp[g >> 1][2 * (g & 1) + 1] = pack2<F16>(pv[2], pv[3]);
         dSp[g >> 1][2 * (g & 1)] = pack2<F16>(dsv[0], dsv[1]);
         dSp[g >> 1][2 * (g & 1) + 1] = pack2<F16>(dsv[2], dsv[3]);
       }
+      pv_block<D, 32, F16, 2, QO + QT>(sq, Pp, dVt, ad);
       // dS^T [key][query] for the dQ product: lane's key row, queries 32 qb + 8 g + 4 hi + 0..3
       if constexpr (ATOMIC_DQ) {
         const int kr = 32 * wave + (lane & 31);
