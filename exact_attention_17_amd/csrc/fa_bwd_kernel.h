@@ -484,10 +484,13 @@ fa_bwd_dq_pass_kernel(BwdArgs a) {
   const int lin = xcd * per + min(xcd, rem) + (w >> 3);
   const int qi = lin % n_qtiles;
   const int qt = CAUSAL ? n_qtiles - 1 - qi : qi;
-  const int hb = lin / n_qtiles;  // head-major, as in the forward
-  const int b = hb % a.batch;
-  const int h = hb / a.batch;
-  const int hk = h / a.group;
+  // (K/V head, sequence, head in group, query tile), as in the forward
+  const int ght = lin / n_qtiles;
+  const int gi = ght % a.group;
+  const int hkb = ght / a.group;
+  const int b = hkb % a.batch;
+  const int hk = hkb / a.batch;
+  const int h = hk * a.group + gi;
 
   int nq, nk;
   int64_t qrow0, krow0;

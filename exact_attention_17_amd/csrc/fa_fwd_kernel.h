@@ -479,13 +479,16 @@ fa_fwd_kernel(FaArgs a) {
   const int qi = lt % a.n_qtiles;
   // under the causal mask the work of a query tile grows with its index: start the longest
   const int qt = a.causal ? a.n_qtiles - 1 - qi : qi;
-  // head-major: an XCD's contiguous range covers a few heads of every sequence, so packed
+  // head-major: an XCD's contiguous range covers a few K/V heads of every sequence, so packed
   // sequences of different lengths spread evenly over the XCDs, while the query tiles of one
-  // (sequence, head) stay together and share that XCD's L2 for their K/V
-  const int hb = lt / a.n_qtiles;
-  const int b = hb % a.batch;
-  const int h = hb / a.batch;
-  const int hk = h / a.group;  // the K/V head this query head reads
+  // (sequence, K/V head) -- of all the query heads that share it -- stay together and share
+  // that XCD's L2 for their K/V.  Order: (K/V head, sequence, head in group, query tile).
+  const int ght = lt / a.n_qtiles;
+  const int gi = ght % a.group;
+  const int hkb = ght / a.group;
+  const int b = hkb % a.batch;
+  const int hk = hkb / a.batch;  // the K/V head this query head reads
+  const int h = hk * a.group + gi;
 
   int nq, nk;
   int64_t qrow0, krow0;
