@@ -46,6 +46,31 @@ WORKLOAD_NAMES = {
 }
 
 
+def device_peak():
+    """Dense bf16 MFMA peak from the device's own CU count and maximum clock (rocminfo), as
+    CUs x 4 SIMD x 1024 FLOP/clk x clock; None when rocminfo is unavailable."""
+    import subprocess
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    cus = clock = None
+    in_gpu = False
+    for line in txt.splitlines():
+        line = line.strip()
+        if line.startswith("Name:") and "gfx" in line:
+            in_gpu = True
+        elif in_gpu and line.startswith("Max Clock Freq. (MHz):"):
+            clock = int(line.split(":")[1].split()[0])
+        elif in_gpu and line.startswith("Compute Unit:"):
+            cus = int(line.split(":")[1].split()[0])
+        if cus and clock:
+            break
+    if not (cus and clock):
+        return None
+    return {"cus": cus, "max_clock_mhz": clock, "peak_tflops": round(cus * 4 * 1024 * clock * 1e6 / 1e12, 1)}
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -223,15 +248,17 @@ def main():
         step()
     torch.cuda.synchronize()
     # Timed region: events on the stream the kernel is launched on.
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # (an event between launches as well, for the per-launch median and minimum)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         step()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_launch = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     tflops = flops / (ms * 1e-3) / 1e12
     log("%s %s: %.4f ms per step (wall %.4f ms), %.1f TFLOP/s, %.1f%% of %.1f, forward tiles %r, splits %d"
         % (args.workload, args.which, ms, wall * 1e3 / args.steps, tflops, 100 * tflops / PEAK_BF16_TFLOPS,
@@ -275,6 +302,8 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": nbytes,
                      "algorithmic_flops": flops},
         "cpu_baseline": cpu,
+        "launch_ms": {"median": round(per_launch[len(per_launch) // 2], 5), "min": round(per_launch[0], 5)},
+        "device_peak": device_peak(),
     }
     print(json.dumps(out), flush=True)
 
