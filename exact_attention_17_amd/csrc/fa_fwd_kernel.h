@@ -32,9 +32,10 @@
 //  * LDS rows are XOR-swizzled in 16-byte chunks so that both the K reads
 //    (16 B per lane, 32 rows) and the transposed V reads (8 B per lane,
 //    8 rows x 4 chunks) spread over all banks.
-//  * Workgroups are renumbered so that the query tiles of one (batch, head)
-//    run on the same XCD and share its L2 for K/V; an XCD's range runs over
-//    heads first, so every XCD gets a share of every (packed) sequence.
+//  * Workgroups are renumbered so that the query tiles of one (batch, K/V
+//    head), over all the query heads that share it, run on the same XCD and
+//    share its L2 for K/V; an XCD's range runs over K/V heads first, so every
+//    XCD gets a share of every (packed) sequence.
 //
 // Schedules:
 //  SCHED 0: each wavefront owns one 32-row block and runs QK^T, softmax and
