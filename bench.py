@@ -75,17 +75,42 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def _code_only(text):
+    """C++ source with comments and whitespace removed (string literals kept), so that
+    editing a comment does not count as a kernel change."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"':
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            i = text.find("*/", i + 2)
+            i = n if i < 0 else i + 2
+        else:
+            if not c.isspace():
+                out.append(c)
+            i += 1
+    return "".join(out)
+
+
 def kernel_source_hash():
     """Hash of the forward kernel's device sources (the kernel template, the shared argument
-    header and the instantiation units); counter-derived traffic is only reported for the
-    same kernel."""
+    header and the instantiation units), comments and whitespace aside; counter-derived
+    traffic is only reported for the same kernel."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "exact_attention_17_amd", "csrc", "*"))):
         base = os.path.basename(p)
         if base == "fa_internal.h" or (base.startswith("fa_fwd_") and base.endswith((".h", ".hip"))):
-            with open(p, "rb") as f:
-                h.update(os.path.basename(p).encode())
-                h.update(f.read())
+            with open(p, encoding="utf-8") as f:
+                h.update(base.encode())
+                h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
