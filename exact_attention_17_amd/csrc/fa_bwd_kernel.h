@@ -198,6 +198,14 @@ __device__ __forceinline__ void store_rows(const f32x16 (&A)[D / 32], float mul,
   }
 }
 
+// The lane's index within its wavefront, recomputed where it is called (the asm is opaque, so
+// values derived from it are neither hoisted out of a loop nor kept live across one).
+__device__ __forceinline__ int fresh_lane_id() {
+  int l;
+  __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // BKV = 32 * NW keys per workgroup, BQ = 64 query rows per step (two 32-row blocks).
 // ATOMIC_DQ: also form dQ = dS K here and add it into the fp32 accumulator with atomics (the
 // pages' Algorithm 2); otherwise dQ is left to fa_bwd_dq_pass_kernel.
@@ -276,8 +284,12 @@ fa_bwd_kernel(BwdArgs a) {
   // The K tile to LDS (B operand of dQ, read transposed), swizzled like the forward's tiles.
   auto load_rows = [&](const __amdgpu_buffer_rsrc_t &rsrc, char *dst, int row0, uint32_t row_bytes, int nch)
                        __attribute__((always_inline)) {
+    // the lane id is fetched afresh: offsets recomputed per call cost a few VALU, while
+    // offsets kept live across the step loop get spilled, and a reload waits for every
+    // load in flight (the prefetch included)
+    const int ln = fresh_lane_id();
     for (int u = wave; u < nch; u += NW) {
-      const int pos = u * 1024 + lane * 16;
+      const int pos = u * 1024 + ln * 16;
       const int r = pos / ROWB;
       const int cc = ((pos % ROWB) >> 4) ^ swz<D>(r);
       const uint32_t goff = (uint32_t)(row0 + r) * row_bytes + cc * 16;
@@ -303,7 +315,6 @@ fa_bwd_kernel(BwdArgs a) {
     dKt[dt] = f32x16{};
     dVt[dt] = f32x16{};
   }
-  const LdsAddr ad = lds_addr<D>(lane);
   const LdsAddr ads = lds_addr<BQ>(lane);  // transposed reads of dS^T (rows of BQ queries)
   const float c = a.scale_log2;
 
@@ -327,10 +338,10 @@ fa_bwd_kernel(BwdArgs a) {
     const int64_t vrow = ((int64_t)b * a.heads + h) * a.seqlen_q;
     if (wave == 0) {
       const auto rl = make_rsrc(a.lse2 + vrow, (uint32_t)nq * 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (void FA_LDS *)sv, 4, (uint32_t)(q0 + lane) * 4, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (void FA_LDS *)sv, 4, (uint32_t)(q0 + fresh_lane_id()) * 4, 0, 0, 0);
     } else if (wave == 1) {
       const auto rd = make_rsrc(a.dvec + vrow, (uint32_t)nq * 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (void FA_LDS *)(sv + VT), 4, (uint32_t)(q0 + lane) * 4, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (void FA_LDS *)(sv + VT), 4, (uint32_t)(q0 + fresh_lane_id()) * 4, 0, 0, 0);
     }
   };
 
@@ -354,6 +365,8 @@ fa_bwd_kernel(BwdArgs a) {
     const int h = hk * a.group + s / nqt_w;
     const int q0 = (qt0 + s % nqt_w) * BQ;
     const char *sq = sqd + (s & 1) * 2 * QT;  // Q of this stage, dO after it
+    const int fl = fresh_lane_id();  // per step, for the reason above
+    const LdsAddr ad = lds_addr<D>(fl);
     const float *sl2 = (const float *)(svec + (s & 1) * 2 * VT);
     const float *sdv = sl2 + BQ;
 
@@ -364,12 +377,12 @@ fa_bwd_kernel(BwdArgs a) {
       // (shorter read lookahead than the forward's: two wavefronts per SIMD hide latency and
       // the registers are needed for dK and dV; S and dP back to back, then P and dS, then
       // the two accumulating products: more independent work than forming dP after dV)
-      qk_block<D, 32, F16, 3, QO>(sq, S, kreg, ad);
-      qk_block<D, 32, F16, 3, QO + QT>(sq, dP, vreg, ad);
+      qk_block<D, 32, F16, 2, QO>(sq, S, kreg, ad);
+      qk_block<D, 32, F16, 2, QO + QT>(sq, dP, vreg, ad);
       // rows of this lane: query q0 + 32 qb + 8 g + 4 hi + r; L log2(e) and D are read from
       // LDS four rows at a time, and P and dS packed to 16 bits as they are formed
-      const int rb = 32 * qb + 4 * hi;
-      const int qrow_base = q0 + rb;
+      const int rb = 32 * qb + 4 * (fl >> 5);
+      const int kq = my_key - (q0 + rb);  // (causal) masked where kq > 8 g + r
       i32x4 Pp[2], dSp[2];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -382,7 +395,7 @@ fa_bwd_kernel(BwdArgs a) {
           float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[0][e], c, -l2[r]));
           // masked: (causal) key past the query; with the atomic dQ also a key past the
           // sequence, whose zero K row would otherwise meet an unbounded P in dS K
-          if ((ATOMIC_DQ && my_key >= nk) || (CAUSAL && my_key > qrow_base + 8 * g + r)) p = 0.f;
+          if ((ATOMIC_DQ && my_key >= nk) || (CAUSAL && kq > 8 * g + r)) p = 0.f;
           pv[r] = p;
           dsv[r] = p * (dP[0][e] - dd[r]);
         }
