@@ -85,8 +85,7 @@ int log2_bucket(int n) {
 
 // Built-in choice, from sweeps of the compiled configurations on MI355X: a short query
 // tile gains nothing from more wavefronts; at d_head 128 and longer sequences eight
-// wavefronts sharing one K/V stream per CU are fastest, except under the causal mask, where
-// the 128-row tile's narrower diagonal band (fewer partly idle wavefronts) wins by about 2%;
+// wavefronts sharing one K/V stream per CU are fastest, except under the causal mask (below);
 // otherwise two workgroups of four.
 fa_tile_config_t default_config(int seqlen_q, int d, bool causal) {
   if (seqlen_q <= 64) return fa_tile_config_t{64, 64, 2, 2, 0};
