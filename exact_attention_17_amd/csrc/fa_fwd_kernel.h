@@ -95,6 +95,7 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // The running max used as the exponent reference moves only when a tile's row max exceeds
 // it by more than this many powers of two (so unnormalised terms stay below 2^8).
 constexpr float kLazyRescale = 8.0f;
+constexpr float kLazyBound = 256.0f;  // 2^kLazyRescale
 // Dword 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle).
 constexpr int kBufferFlags = 0x00020000;
 
@@ -352,6 +353,64 @@ __device__ __forceinline__ float softmax_block(f32x16 (&S)[BC / 32], i32x4 (&P)[
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         P[2 * kb + s2][e] = pack2<F16>(S[kb][8 * s2 + 2 * e], S[kb][8 * s2 + 2 * e + 1]);
+  return alpha;
+}
+
+// The same step for a tile with no masked key, speculating that the reference max stays:
+// the exponentials are first taken against the current m.  If every lane's partial sum of
+// them is at most 2^kLazyRescale, so is each of them (all are >= 0), so no row's max moved
+// by more than kLazyRescale and the step above would have kept m: the result is then bit
+// for bit the same (same products, same order of sums, alpha = 1).  Otherwise (in
+// particular on a row's first tile, where m = -inf makes the sum +inf or NaN) the step
+// above is taken from the scores, into the same registers.  The row max and its exchange
+// between lanes leave the common path.
+template <int BC, bool F16>
+__device__ __forceinline__ float softmax_block_spec(const f32x16 (&S)[BC / 32], i32x4 (&P)[BC / 16], float &m,
+                                                    float &l, float c, bool &rescale) {
+  constexpr int KB = BC / 32;
+  f32x16 E[KB];
+  float mc = m * c;
+  float rs = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      E[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], c, -mc));
+      rs += E[kb][r];
+    }
+  float alpha = 1.f;
+  rescale = false;
+  if (__builtin_amdgcn_ballot_w64(!(rs <= kLazyBound)) != 0) {
+    float mx = S[0][0];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
+    mx = pair_max(mx);
+    const bool grow = (mx - m) * c > kLazyRescale;
+    const float m_new = grow ? mx : m;
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    alpha = __builtin_amdgcn_exp2f((m - m_ref) * c);
+    rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
+    m = m_new;
+    mc = m_ref * c;
+    rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        E[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], c, -mc));
+        rs += E[kb][r];
+      }
+  }
+  l = l * alpha + rs;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        P[2 * kb + s2][e] = pack2<F16>(E[kb][8 * s2 + 2 * e], E[kb][8 * s2 + 2 * e + 1]);
   return alpha;
 }
 
@@ -654,8 +713,11 @@ fa_fwd_kernel(FaArgs a) {
         constexpr bool IMM = SO + STAGE <= 65536;
         const char *base = IMM ? smem : smem + SO;
         qk_block<D, BC, F16, QK_LA, IMM ? SO : 0>(base, S, qreg[0], ad);
+        // (schedule 4 keeps the plain step: the speculative one's extra registers spill there)
         const float alpha =
-            softmax_block<BC, F16, MK>(S, P, m[0], l[0], c, MK ? klim[0] - (jb + j) * BC - 4 * hi : 0, rs);
+            MK || SCHED == 4
+                ? softmax_block<BC, F16, MK>(S, P, m[0], l[0], c, MK ? klim[0] - (jb + j) * BC - 4 * hi : 0, rs)
+                : softmax_block_spec<BC, F16>(S, P, m[0], l[0], c, rs);
         if (rs) rescale_o<DT>(O[0], alpha);
         pv_block<D, BC, F16, PV_LA, (IMM ? SO : 0) + TILE>(base, P, O[0], ad);
       }
