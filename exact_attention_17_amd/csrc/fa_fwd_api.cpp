@@ -94,7 +94,9 @@ fa_tile_config_t default_config(int seqlen_q, int d, bool causal) {
     // three four-wavefront workgroups per CU (32-key tiles) then hide more of each step's
     // latency than the eight-wavefront tile does (about 7% on B16 N4096 H16).
     if (causal) return fa_tile_config_t{128, 32, 4, 2, 4};
-    return fa_tile_config_t{256, 64, 8, 2, 0};
+    // Eight wavefronts in the ping-pong schedule: each SIMD's two wavefronts alternate matrix
+    // and softmax halves (3-5% over schedule 0 on full, gqa and varlen).
+    return fa_tile_config_t{256, 64, 8, 3, 2};
   }
   return fa_tile_config_t{128, 64, 4, 2, 0};
 }

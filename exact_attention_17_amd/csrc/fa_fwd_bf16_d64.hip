@@ -13,8 +13,8 @@ void register_bf16_d64(void (*add)(const KernelEntry &)) {
   add(make_entry<64, 256, 64, 8, 2, false>());
   add(make_entry<64, 128, 64, 4, 1, false>());
   add(make_entry<64, 256, 32, 4, 2, false, 1>());
-  add(make_entry<64, 256, 64, 8, 2, false, 2>());
-  add(make_entry<64, 256, 32, 8, 2, false, 2>());
+  add(make_entry<64, 256, 64, 8, 3, false, 2>());
+  add(make_entry<64, 256, 32, 8, 3, false, 2>());
   add(make_entry<64, 256, 32, 8, 2, false>());
   add(make_entry<64, 256, 64, 8, 3, false>());
   add(make_entry<64, 256, 64, 8, 4, false>());

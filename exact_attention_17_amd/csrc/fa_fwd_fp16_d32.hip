@@ -13,8 +13,8 @@ void register_fp16_d32(void (*add)(const KernelEntry &)) {
   add(make_entry<32, 256, 64, 8, 2, true>());
   add(make_entry<32, 128, 64, 4, 1, true>());
   add(make_entry<32, 256, 32, 4, 2, true, 1>());
-  add(make_entry<32, 256, 64, 8, 2, true, 2>());
-  add(make_entry<32, 256, 32, 8, 2, true, 2>());
+  add(make_entry<32, 256, 64, 8, 3, true, 2>());
+  add(make_entry<32, 256, 32, 8, 3, true, 2>());
   add(make_entry<32, 256, 32, 8, 2, true>());
   add(make_entry<32, 256, 64, 8, 3, true>());
   add(make_entry<32, 256, 64, 8, 4, true>());

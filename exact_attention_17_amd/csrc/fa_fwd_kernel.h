@@ -510,13 +510,14 @@ fa_fwd_kernel(FaArgs a) {
   constexpr int DT = D / 32;              // 32-wide d tiles of the output
   constexpr int KB = BC / 32;             // 32-key blocks per tile
   constexpr int KS = BC / 16;             // 16-key MFMA steps per tile
-  // LDS: SCHED 0 holds STAGES (K, V) tile pairs; SCHED 1 a 2-slot K ring and a 3-slot V ring.
-  constexpr int LDS_BYTES = SCHED == 1 ? 5 * TILE : STAGES * 2 * TILE;  // SCHED 2: 2 K + 2 V slots
+  // LDS: SCHED 0 holds STAGES (K, V) tile pairs; SCHED 1 a 2-slot K ring and a 3-slot V ring;
+  // SCHED 2 (STAGES = 3) a 3-slot V ring and a 3-slot K ring.
+  constexpr int LDS_BYTES = SCHED == 1 ? 5 * TILE : STAGES * 2 * TILE;
   static_assert(BR == NW * QW, "rows per workgroup");
   static_assert(D == 32 || D == 64 || D == 128, "d_head");
   static_assert(BC % 32 == 0 && TILE % 1024 == 0, "tile shape");
   static_assert(STAGES >= 1 && STAGES <= 4, "stages");
-  static_assert(SCHED == 0 || (SCHED == 1 && STAGES == 2) || (SCHED == 2 && STAGES == 2 && NW == 8) ||
+  static_assert(SCHED == 0 || (SCHED == 1 && STAGES == 2) || (SCHED == 2 && STAGES == 3 && NW == 8) ||
                     (SCHED == 4 && BC == 32),
                 "schedule");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
@@ -796,49 +797,73 @@ fa_fwd_kernel(FaArgs a) {
     // wavefront runs the same program, step j = MMA(j) | barrier | SM(j) | barrier, where
     // MMA(j) = PV(j-1) + QK(j) and SM(j) is the softmax of tile j; group 1 starts one
     // barrier later, so on each SIMD (one wavefront of each group) one wavefront issues
-    // matrix instructions while the other runs its softmax.  K(j) and V(j-1) are read in the
-    // two halves around the middle barrier of group 0's step j.  Group 0 issues the loads of
-    // K(j+1) (into K slot (j+1)&1, whose K(j-1) was last read before the barrier that starts
-    // this step) and V(j) (into V slot j&1, holding V(j-2)) at the start of its step j and
-    // waits for them at its end, one barrier before anyone reads them.
+    // matrix instructions while the other runs its softmax.  K and V tiles each have a
+    // 3-slot ring (tile t in slot t % 3; V slots first, then K slots).  With barriers
+    // B0, B1, ... and group 0's step j between B(2j) and B(2j+2): K(j) and V(j-1) are read
+    // between B(2j) and B(2j+2).  Group 0 issues the loads of K(j+2) (into the slot of
+    // K(j-1)) and V(j+1) (into the slot of V(j-2)), both last read before B(2j), in its
+    // softmax half of step j, after B(2j+1), and waits for the previous step's loads (K(j+1),
+    // V(j)) before B(2j+2), one barrier ahead of their first reads; the matrix halves issue
+    // no loads.
     const int grp = wave >> 2;
     const int gw = wave & 3;
     using Four = std::integral_constant<int, 4>;
+    constexpr int LPG = 2 * (NCH >= 4 ? NCH / 4 : 1);  // loads per step of a group-0 wavefront
+    static_assert(NCH % 4 == 0 || 4 % NCH == 0, "tile pieces spread evenly");
     f32x16 S[KB];
     i32x4 P[KS];
-    auto kslot = [&](int j) __attribute__((always_inline)) { return smem + (j & 1) * TILE; };
-    auto vslot = [&](int j) __attribute__((always_inline)) { return smem + 2 * TILE + (j & 1) * TILE; };
-    if (ntl > 0) load_one(rk, kslot(0), jb);
+    char *const kbase = smem + 3 * TILE;  // K slots; V slots at smem
+    for (int t = 0; t < 2; ++t)
+      if (t < ntl) load_one(rk, kbase + t * TILE, jb + t);
+    if (ntl > 0) load_one(rv, smem, jb);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     wg_barrier();
     if (grp == 1) wg_barrier();
-    // One instance of the loop when no tile of the wavefront needs the mask (the usual case
-    // without the causal mask), so that the unmasked softmax is straight-line code; the
-    // other chooses per tile.
-    auto loop = [&](auto mask_c) __attribute__((always_inline)) {
-      constexpr bool ANY = decltype(mask_c)::value;
-      for (int j = 0; j <= ntl; ++j) {
-        if (grp == 0) {
-          if (j + 1 < ntl) load_by(rk, kslot(j + 1), jb + j + 1, gw, Four{});
-          if (j < ntl) load_by(rv, vslot(j), jb + j, gw, Four{});
-        }
-        if (j >= 1) pv_block<D, BC, F16>(vslot(j - 1), P, O[0], ad);
-        if (j < ntl) qk_block<D, BC, F16>(kslot(j), S, qreg[0], ad);
-        wg_barrier();
-        if (j < ntl) {
-          bool rs;
-          const float alpha =
-              ANY ? softmax(S, P, 0, jb + j, rs) : softmax_block<BC, F16, false>(S, P, m[0], l[0], c, 0, rs);
-          if (rs) rescale_o<DT>(O[0], alpha);
-        }
-        if (grp == 0) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        wg_barrier();
+    // Step j in slot ST = j % 3 (a compile-time index, so that slot offsets are immediates);
+    // steps j >= ntl only finish PV(j - 1).
+    auto step = [&](auto st_c, auto mask_c, int j) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st_c)::value;
+      constexpr bool MK = decltype(mask_c)::value;
+      constexpr int SP = (ST + 2) % 3;  // slot of tile j - 1 (and of tile j + 2)
+      constexpr int SN = (ST + 1) % 3;  // slot of tile j + 1
+      if (j >= 1) pv_block<D, BC, F16, 4, SP * TILE>(smem, P, O[0], ad);
+      if (j < ntl) qk_block<D, BC, F16, 6, ST * TILE>(kbase, S, qreg[0], ad);
+      wg_barrier();
+      if (grp == 0) {
+        if (j + 2 < ntl) load_by(rk, kbase + SP * TILE, jb + j + 2, gw, Four{});
+        if (j + 1 < ntl) load_by(rv, smem + SN * TILE, jb + j + 1, gw, Four{});
+      }
+      if (j < ntl) {
+        bool rs;
+        const float alpha =
+            MK ? softmax_block<BC, F16, true>(S, P, m[0], l[0], c, klim[0] - (jb + j) * BC - 4 * hi, rs)
+               : softmax_block_spec<BC, F16>(S, P, m[0], l[0], c, rs);
+        if (rs) rescale_o<DT>(O[0], alpha);
+      }
+      if (grp == 0) {
+        // K(j+1) and V(j) landed; this step's loads may still be in flight
+        if (j + 2 < ntl)
+          wait_vmcnt<LPG>();
+        else if (j + 1 < ntl)
+          wait_vmcnt<LPG / 2>();
+        else
+          wait_vmcnt<0>();
+      }
+      wg_barrier();
+    };
+    // Steps [0, jm) take tiles with no masked key, steps [jm, ntl] the others (and the last
+    // step, PV only), each range in a loop of its own, as in schedule 0.
+    const int jm = min(max(kfull[0] - jb, 0), ntl);
+    auto run = [&](auto mask_c, int j0, int j1) __attribute__((always_inline)) {
+      for (int jj = j0 - j0 % 3; jj < j1; jj += 3) {
+        static_for<0, 3>([&](auto st_c) __attribute__((always_inline)) {
+          const int j = jj + decltype(st_c)::value;
+          if (j >= j0 && j < j1) step(st_c, mask_c, j);
+        });
       }
     };
-    if (kfull[0] - jb >= ntl)
-      loop(std::false_type{});
-    else
-      loop(std::true_type{});
+    run(std::false_type{}, 0, jm);
+    run(std::true_type{}, jm, ntl + 1);
     if (grp == 0) wg_barrier();
     finish(0);
   }

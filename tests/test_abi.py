@@ -96,7 +96,7 @@ def test_config_registry_host_only():
                     assert fa.fa_fwd_config_lds_bytes(d, c) == 5 * tile
                 else:
                     if c.schedule == 2:
-                        assert c.waves == 8 and c.stages == 2
+                        assert c.waves == 8 and c.stages == 3
                     assert c.br == 32 * c.waves
                     assert fa.fa_fwd_config_lds_bytes(d, c) == c.stages * 2 * tile
                 assert fa.fa_fwd_config_lds_bytes(d, c) <= 160 * 1024
@@ -108,7 +108,7 @@ def test_config_registry_host_only():
 
 def test_default_and_forced_config():
     c = fa.fa_fwd_get_config(16, 4096, 4096, 16, 128, fa.FA_BF16)
-    assert c.as_tuple() == (256, 64, 8, 2, 0)
+    assert c.as_tuple() == (256, 64, 8, 3, 2)
     small = fa.fa_fwd_get_config(1, 64, 4096, 1, 128, fa.FA_BF16)
     assert small.br == 64
     with pytest.raises(fa.FaError):
@@ -120,7 +120,7 @@ def test_default_and_forced_config():
         assert fa.fa_fwd_get_config(16, 4096, 4096, 16, 64, fa.FA_BF16).as_tuple() == (128, 64, 4, 2, 0)
     finally:
         fa.fa_fwd_set_config(128, fa.FA_BF16, None)
-    assert fa.fa_fwd_get_config(16, 4096, 4096, 16, 128, fa.FA_BF16).as_tuple() == (256, 64, 8, 2, 0)
+    assert fa.fa_fwd_get_config(16, 4096, 4096, 16, 128, fa.FA_BF16).as_tuple() == (256, 64, 8, 3, 2)
 
 
 def test_causal_default_config():

@@ -207,7 +207,7 @@ def test_repeat_launches_bitwise_identical():
 
 
 @pytest.mark.parametrize("ref,alt", [((256, 32, 8, 2, 0), (256, 32, 4, 2, 1)),
-                                     ((256, 64, 8, 2, 0), (256, 64, 8, 2, 2)),
+                                     ((256, 64, 8, 2, 0), (256, 64, 8, 3, 2)),
                                      ((128, 32, 4, 2, 0), (128, 32, 4, 2, 4))])
 def test_schedules_match_in_order_bitwise_on_ragged_shapes(ref, alt):
     # The dual-block, ping-pong and three-per-SIMD schedules reorder work inside or across
