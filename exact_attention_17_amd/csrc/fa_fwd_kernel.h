@@ -799,16 +799,17 @@ fa_fwd_kernel(FaArgs a) {
     // barrier later, so on each SIMD (one wavefront of each group) one wavefront issues
     // matrix instructions while the other runs its softmax.  K and V tiles each have a
     // 3-slot ring (tile t in slot t % 3; V slots first, then K slots).  With barriers
-    // B0, B1, ... and group 0's step j between B(2j) and B(2j+2): K(j) and V(j-1) are read
-    // between B(2j) and B(2j+2).  Group 0 issues the loads of K(j+2) (into the slot of
-    // K(j-1)) and V(j+1) (into the slot of V(j-2)), both last read before B(2j), in its
-    // softmax half of step j, after B(2j+1), and waits for the previous step's loads (K(j+1),
-    // V(j)) before B(2j+2), one barrier ahead of their first reads; the matrix halves issue
-    // no loads.
+    // B0, B1, ... and group 0's step j between B(2j) and B(2j+2) (group 1's between B(2j+1)
+    // and B(2j+3)): K(j) and V(j-1) are read between B(2j) and B(2j+2).  The loads are
+    // issued in the softmax halves only: group 0 issues K(j+2) (into the slot of K(j-1),
+    // last read before B(2j)) after B(2j+1) and waits for K(j+1) before B(2j+2); group 1
+    // issues V(j+1) (into the slot of V(j-2), last read before B(2j)) after B(2j+2) and waits
+    // for it before B(2j+4), at the end of its next matrix half.  Each wait is one barrier
+    // ahead of the tile's first read.
     const int grp = wave >> 2;
     const int gw = wave & 3;
     using Four = std::integral_constant<int, 4>;
-    constexpr int LPG = 2 * (NCH >= 4 ? NCH / 4 : 1);  // loads per step of a group-0 wavefront
+    constexpr int LPT = NCH >= 4 ? NCH / 4 : 1;  // loads per tile of a loading wavefront
     static_assert(NCH % 4 == 0 || 4 % NCH == 0, "tile pieces spread evenly");
     f32x16 S[KB];
     i32x4 P[KS];
@@ -828,9 +829,11 @@ fa_fwd_kernel(FaArgs a) {
       constexpr int SN = (ST + 1) % 3;  // slot of tile j + 1
       if (j >= 1) pv_block<D, BC, F16, 4, SP * TILE>(smem, P, O[0], ad);
       if (j < ntl) qk_block<D, BC, F16, 6, ST * TILE>(kbase, S, qreg[0], ad);
+      if (grp == 1) wait_vmcnt<0>();  // V(j), issued in the previous step, landed
       wg_barrier();
       if (grp == 0) {
         if (j + 2 < ntl) load_by(rk, kbase + SP * TILE, jb + j + 2, gw, Four{});
+      } else {
         if (j + 1 < ntl) load_by(rv, smem + SN * TILE, jb + j + 1, gw, Four{});
       }
       if (j < ntl) {
@@ -841,11 +844,9 @@ fa_fwd_kernel(FaArgs a) {
         if (rs) rescale_o<DT>(O[0], alpha);
       }
       if (grp == 0) {
-        // K(j+1) and V(j) landed; this step's loads may still be in flight
+        // K(j+1) landed; this step's loads may still be in flight
         if (j + 2 < ntl)
-          wait_vmcnt<LPG>();
-        else if (j + 1 < ntl)
-          wait_vmcnt<LPG / 2>();
+          wait_vmcnt<LPT>();
         else
           wait_vmcnt<0>();
       }
