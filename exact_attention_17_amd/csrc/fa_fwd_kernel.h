@@ -64,7 +64,8 @@
 //    every step into a matrix half (PV of the previous tile, QK^T of this
 //    one) and a softmax half, and the second group runs one half behind the
 //    first: the ping-pong of page "GPU 内核与 FlashAttention", section 15.3,
-//    with one barrier in place of named barriers.
+//    with one barrier in place of named barriers.  The matrix half's two products
+//    form one MFMA stream, so LDS reads for QK^T overlap the end of PV.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -300,6 +301,88 @@ __device__ __forceinline__ void pv_block(const char *sv, const i32x4 (&P)[BC / 1
   });
 }
 
+// Reads still outstanding after those of op I in a stream of N ops whose op k has its reads
+// issued before op k - L: ops I+1 .. min(I+L, N-1), two reads for a PV op (k < NP), one for a
+// QK^T op.
+template <int I, int L, int N, int NP>
+constexpr int pvqk_after() {
+  int n = 0;
+  for (int k = I + 1; k <= I + L && k < N; ++k) n += k < NP ? 2 : 1;
+  return n;
+}
+
+// PV of the previous tile (pv_block) and S^T = K Q^T of this one (qk_block) as one stream of
+// MFMAs with one read lookahead, so that the first K reads are in flight during the last PV
+// MFMAs rather than issued after them.  Same products in the same order as the two
+// functions called in turn.
+template <int D, int BC, bool F16, int LA, int SOFFV, int SOFFK>
+__device__ __forceinline__ void pvqk_block(const char *sv, const i32x4 (&P)[BC / 16], f32x16 (&O)[D / 32],
+                                           const char *sk, f32x16 (&S)[BC / 32], const i32x4 (&qr)[D / 16],
+                                           const LdsAddr &ad) {
+  constexpr int ROWB = D * 2, DT = D / 32, KS = BC / 16, NP = KS * DT, KB = BC / 32, T = D / 16;
+  constexpr int N = NP + T * KB, L = LA;
+  static_assert(2 * L <= 15, "lgkmcnt field");
+  static_assert(SOFFV + 16 * (KS - 1) * ROWB < 65536 && SOFFK + (KB - 1) * 32 * ROWB < 65536,
+                "ds_read offset field");
+  const uint32_t sv_lds = (uint32_t)(uintptr_t)(const char FA_LDS *)sv;
+  const uint32_t sk_lds = (uint32_t)(uintptr_t)(const char FA_LDS *)sk;
+  uint32_t a0[DT], a1[DT], koff[T];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    a0[dt] = sv_lds + (uint32_t)(((64 * dt) ^ ad.vx0) + ad.vbase0);
+    a1[dt] = sv_lds + (uint32_t)(((64 * dt) ^ ad.vx1) + ad.vbase1);
+  }
+#pragma unroll
+  for (int t = 0; t < T; ++t) koff[t] = sk_lds + (uint32_t)(((32 * t) ^ ad.kx) + ad.kbase);
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) S[kb] = f32x16{};
+  i16x4 b0[L + 1], b1[L + 1];
+  i32x4 kbuf[L + 1];
+  auto issue = [&](auto k_c) __attribute__((always_inline)) {
+    constexpr int k = decltype(k_c)::value;
+    if constexpr (k < NP) {
+      lds_read_tr<SOFFV + 16 * (k / DT) * ROWB>(b0[k % (L + 1)], a0[k % DT]);
+      lds_read_tr<SOFFV + 16 * (k / DT) * ROWB>(b1[k % (L + 1)], a1[k % DT]);
+    } else {
+      constexpr int i = k - NP;
+      lds_read_b128<SOFFK + (i % KB) * 32 * ROWB>(kbuf[k % (L + 1)], koff[i / KB]);
+    }
+  };
+  static_for<0, L>(issue);
+  static_for<0, N>([&](auto i_c) __attribute__((always_inline)) {
+    constexpr int i = decltype(i_c)::value;
+    if constexpr (i + L < N) issue(IC<i + L>{});
+    lds_wait<pvqk_after<i, L, N, NP>()>();
+    if constexpr (i < NP) {
+      lds_dep(b0[i % (L + 1)]);
+      lds_dep(b1[i % (L + 1)]);
+      const i16x4 &v0 = b0[i % (L + 1)], &v1 = b1[i % (L + 1)];
+      const i16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      O[i % DT] = mfma32<F16>(__builtin_bit_cast(i32x4, va), P[i / DT], O[i % DT]);
+    } else {
+      constexpr int q = i - NP;
+      lds_dep(kbuf[i % (L + 1)]);
+      S[q % KB] = mfma32<F16>(kbuf[i % (L + 1)], qr[q / KB], S[q % KB]);
+    }
+  });
+}
+
+// A lane's share of a row sum over one tile.  With 64 or more keys per tile (32 or more
+// terms per lane) it is accumulated in four interleaved partial sums (register r of each
+// 16-register block goes to sum r % 4), added pairwise at the end: four short chains of
+// dependent adds instead of one long one (about 0.5 % on the ping-pong schedule).  With 32-key
+// tiles it is one chain: the three-wavefront-per-SIMD schedule ran 0.7 % slower with four.
+template <int KB>
+struct RowSum {
+  static constexpr int NP = KB >= 2 ? 4 : 1;
+  float v[NP] = {};
+  __device__ __forceinline__ void add(int r, float x) { v[r % NP] += x; }
+  __device__ __forceinline__ float total() const {
+    if constexpr (NP == 4) return (v[0] + v[1]) + (v[2] + v[3]);
+    return v[0];
+  }
+};
+
 // Online softmax step of one 32-query block on the raw scores S of tile j (keys from
 // kvalid on, when MASK, are past the sequence end).  Leaves P~ (16-bit PV operands) in P,
 // updates m and l, and returns alpha, the factor O must be multiplied by before this tile's
@@ -336,16 +419,16 @@ __device__ __forceinline__ float softmax_block(f32x16 (&S)[BC / 32], i32x4 (&P)[
   rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
   m = m_new;
   const float mc = m_ref * c;
-  float rs = 0.f;
+  RowSum<KB> rs;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], c, -mc));
       S[kb][r] = p;
-      rs += p;
+      rs.add(r, p);
     }
-  l = l * alpha + rs;
+  l = l * alpha + rs.total();
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -370,14 +453,15 @@ __device__ __forceinline__ float softmax_block_spec(const f32x16 (&S)[BC / 32], 
   constexpr int KB = BC / 32;
   f32x16 E[KB];
   float mc = m * c;
-  float rs = 0.f;
+  RowSum<KB> part;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       E[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], c, -mc));
-      rs += E[kb][r];
+      part.add(r, E[kb][r]);
     }
+  float rs = part.total();
   float alpha = 1.f;
   rescale = false;
   if (__builtin_amdgcn_ballot_w64(!(rs <= kLazyBound)) != 0) {
@@ -394,14 +478,15 @@ __device__ __forceinline__ float softmax_block_spec(const f32x16 (&S)[BC / 32], 
     rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
     m = m_new;
     mc = m_ref * c;
-    rs = 0.f;
+    RowSum<KB> again;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         E[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], c, -mc));
-        rs += E[kb][r];
+        again.add(r, E[kb][r]);
       }
+    rs = again.total();
   }
   l = l * alpha + rs;
 #pragma unroll
@@ -820,15 +905,24 @@ fa_fwd_kernel(FaArgs a) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     wg_barrier();
     if (grp == 1) wg_barrier();
-    // Step j in slot ST = j % 3 (a compile-time index, so that slot offsets are immediates);
-    // steps j >= ntl only finish PV(j - 1).
-    auto step = [&](auto st_c, auto mask_c, int j) __attribute__((always_inline)) {
+    // Step j in slot ST = j % 3 (a compile-time index, so that slot offsets are immediates).
+    // Phase PH: 0 for step 0 (QK^T only), 1 for steps 1 .. ntl-1 (PV and QK^T as one MFMA
+    // stream), 2 for step ntl (PV only).  The first and last steps run outside the loops, so
+    // that the loop body has no branch around its matrix products (with one, the registers
+    // of both paths met at the join and the kernel spilled).
+    auto step = [&](auto st_c, auto mask_c, auto ph_c, int j) __attribute__((always_inline)) {
       constexpr int ST = decltype(st_c)::value;
       constexpr bool MK = decltype(mask_c)::value;
+      constexpr int PH = decltype(ph_c)::value;
       constexpr int SP = (ST + 2) % 3;  // slot of tile j - 1 (and of tile j + 2)
       constexpr int SN = (ST + 1) % 3;  // slot of tile j + 1
-      if (j >= 1) pv_block<D, BC, F16, 4, SP * TILE>(smem, P, O[0], ad);
-      if (j < ntl) qk_block<D, BC, F16, 6, ST * TILE>(kbase, S, qreg[0], ad);
+      if constexpr (PH == 1) {
+        pvqk_block<D, BC, F16, 5, SP * TILE, ST * TILE>(smem, P, O[0], kbase, S, qreg[0], ad);
+      } else if constexpr (PH == 0) {
+        qk_block<D, BC, F16, 6, ST * TILE>(kbase, S, qreg[0], ad);
+      } else {
+        pv_block<D, BC, F16, 4, SP * TILE>(smem, P, O[0], ad);
+      }
       if (grp == 1) wait_vmcnt<0>();  // V(j), issued in the previous step, landed
       wg_barrier();
       if (grp == 0) {
@@ -836,7 +930,7 @@ fa_fwd_kernel(FaArgs a) {
       } else {
         if (j + 1 < ntl) load_by(rv, smem + SN * TILE, jb + j + 1, gw, Four{});
       }
-      if (j < ntl) {
+      if constexpr (PH != 2) {
         bool rs;
         const float alpha =
             MK ? softmax_block<BC, F16, true>(S, P, m[0], l[0], c, klim[0] - (jb + j) * BC - 4 * hi, rs)
@@ -852,19 +946,34 @@ fa_fwd_kernel(FaArgs a) {
       }
       wg_barrier();
     };
-    // Steps [0, jm) take tiles with no masked key, steps [jm, ntl] the others (and the last
-    // step, PV only), each range in a loop of its own, as in schedule 0.
+    // Steps [1, jm) take tiles with no masked key, steps [jm, ntl) the others, each range in
+    // a loop of its own, as in schedule 0.  With no tile at all (an empty split) there is no
+    // step; both groups still pass the same number of barriers.
     const int jm = min(max(kfull[0] - jb, 0), ntl);
     auto run = [&](auto mask_c, int j0, int j1) __attribute__((always_inline)) {
       for (int jj = j0 - j0 % 3; jj < j1; jj += 3) {
         static_for<0, 3>([&](auto st_c) __attribute__((always_inline)) {
           const int j = jj + decltype(st_c)::value;
-          if (j >= j0 && j < j1) step(st_c, mask_c, j);
+          if (j >= j0 && j < j1) step(st_c, mask_c, IC<1>{}, j);
         });
       }
     };
-    run(std::false_type{}, 0, jm);
-    run(std::true_type{}, jm, ntl + 1);
+    if (ntl > 0) {
+      if (jm > 0)
+        step(IC<0>{}, std::false_type{}, IC<0>{}, 0);
+      else
+        step(IC<0>{}, std::true_type{}, IC<0>{}, 0);
+      run(std::false_type{}, 1, jm);
+      run(std::true_type{}, max(jm, 1), ntl);
+      // the last step's slot, ntl % 3, as a compile-time index
+      const int sl = ntl % 3;
+      if (sl == 0)
+        step(IC<0>{}, std::true_type{}, IC<2>{}, ntl);
+      else if (sl == 1)
+        step(IC<1>{}, std::true_type{}, IC<2>{}, ntl);
+      else
+        step(IC<2>{}, std::true_type{}, IC<2>{}, ntl);
+    }
     if (grp == 0) wg_barrier();
     finish(0);
   }
