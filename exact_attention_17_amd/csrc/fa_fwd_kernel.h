@@ -936,6 +936,12 @@ fa_fwd_kernel(FaArgs a) {
             MK ? softmax_block<BC, F16, true>(S, P, m[0], l[0], c, klim[0] - (jb + j) * BC - 4 * hi, rs)
                : softmax_block_spec<BC, F16>(S, P, m[0], l[0], c, rs);
         if (rs) rescale_o<DT>(O[0], alpha);
+        // The 16-bit P~ and the running sum are formed here, in the softmax half: left to
+        // itself the compiler sank their conversions past the barrier, into the start of
+        // the next matrix half, ahead of its first LDS reads.
+#pragma unroll
+        for (int i = 0; i < KS; ++i) lds_dep(P[i]);
+        lds_dep(l[0]);
       }
       if (grp == 0) {
         // K(j+1) landed; this step's loads may still be in flight
