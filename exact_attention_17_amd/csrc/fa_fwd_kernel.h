@@ -320,7 +320,7 @@ __device__ __forceinline__ void pvqk_block(const char *sv, const i32x4 (&P)[BC /
                                            const char *sk, f32x16 (&S)[BC / 32], const i32x4 (&qr)[D / 16],
                                            const LdsAddr &ad) {
   constexpr int ROWB = D * 2, DT = D / 32, KS = BC / 16, NP = KS * DT, KB = BC / 32, T = D / 16;
-  constexpr int N = NP + T * KB, L = LA;
+  constexpr int N = NP + T * KB, L = LA < N ? LA : N;
   static_assert(2 * L <= 15, "lgkmcnt field");
   static_assert(SOFFV + 16 * (KS - 1) * ROWB < 65536 && SOFFK + (KB - 1) * 32 * ROWB < 65536,
                 "ds_read offset field");
@@ -367,16 +367,17 @@ __device__ __forceinline__ void pvqk_block(const char *sv, const i32x4 (&P)[BC /
   });
 }
 
-// A lane's share of a row sum over one tile.  With 64 or more keys per tile (32 or more
-// terms per lane) it is accumulated in four interleaved partial sums (register r of each
-// 16-register block goes to sum r % 4), added pairwise at the end: four short chains of
-// dependent adds instead of one long one (about 0.5 % on the ping-pong schedule).  With 32-key
-// tiles it is one chain: the three-wavefront-per-SIMD schedule ran 0.7 % slower with four.
+// A lane's share of a row sum over one tile, term i being accumulator register i % 16 of
+// 32-key block i / 16.  With 64 or more keys per tile (32 or more terms per lane) it is
+// accumulated in four interleaved partial sums (term i goes to sum i % 4), added pairwise at
+// the end: four short chains of dependent adds instead of one long one (about 0.5 % on the
+// ping-pong schedule).  With 32-key tiles it is one chain: the three-wavefront-per-SIMD
+// schedule ran 0.7 % slower with four.
 template <int KB>
 struct RowSum {
   static constexpr int NP = KB >= 2 ? 4 : 1;
   float v[NP] = {};
-  __device__ __forceinline__ void add(int r, float x) { v[r % NP] += x; }
+  __device__ __forceinline__ void add(int i, float x) { v[i % NP] += x; }
   __device__ __forceinline__ float total() const {
     if constexpr (NP == 4) return (v[0] + v[1]) + (v[2] + v[3]);
     return v[0];
@@ -426,7 +427,7 @@ __device__ __forceinline__ float softmax_block(f32x16 (&S)[BC / 32], i32x4 (&P)[
     for (int r = 0; r < 16; ++r) {
       const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], c, -mc));
       S[kb][r] = p;
-      rs.add(r, p);
+      rs.add(16 * kb + r, p);
     }
   l = l * alpha + rs.total();
 #pragma unroll
@@ -459,7 +460,7 @@ __device__ __forceinline__ float softmax_block_spec(const f32x16 (&S)[BC / 32], 
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       E[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], c, -mc));
-      part.add(r, E[kb][r]);
+      part.add(16 * kb + r, E[kb][r]);
     }
   float rs = part.total();
   float alpha = 1.f;
@@ -484,7 +485,7 @@ __device__ __forceinline__ float softmax_block_spec(const f32x16 (&S)[BC / 32], 
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         E[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], c, -mc));
-        again.add(r, E[kb][r]);
+        again.add(16 * kb + r, E[kb][r]);
       }
     rs = again.total();
   }
