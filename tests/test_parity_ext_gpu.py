@@ -143,6 +143,15 @@ def test_grouped_heads_small_d(d, dtype):
     check_dense(q, k, v, d ** -0.5, "gqa H6 Hkv3 d%d" % d)
 
 
+@pytest.mark.parametrize("batch,heads,heads_kv", [(5, 8, 2), (2, 4, 4), (7, 3, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_d_sequence_major_order(batch, heads, heads_kv, causal):
+    # dense d_head 32 calls number their work sequence-outermost: cover more sequences than
+    # K/V heads, as many, and fewer, with grouped heads and a ragged query tile
+    q, k, v = inputs.dense_qkv(batch, 150, 150, heads, 32, "bf16", seed=batch * 10 + heads_kv, heads_kv=heads_kv)
+    check_dense(q, k, v, 32 ** -0.5, "d32 B%d H%d Hkv%d" % (batch, heads, heads_kv), causal=causal)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_grouped_heads_varlen(causal):
     check_varlen([1, 130, 0, 64, 300], 8, 2, 128, "bf16", 41, "gqa varlen", causal=causal)
