@@ -1,0 +1,69 @@
+"""Host-side behaviour of bench.py (no GPU): the one-GPU refusal, the kernel-source hash that
+gates counter-derived traffic, and the committed traffic summaries it reads."""
+import glob
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr
+
+
+def test_code_only_drops_comments_and_whitespace_but_not_strings():
+    src = 'int a = 1;  // note\n/* block\n comment */ f("x // y", \'c\');\n'
+    assert bench._code_only(src) == 'inta=1;f("x // y",\'c\');'
+
+
+def test_comment_edits_keep_the_hash(tmp_path, monkeypatch):
+    csrc = tmp_path / "exact_attention_17_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (csrc / "fa_fwd_kernel.h").write_text("int k() { return 1; }\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h1 = bench.kernel_source_hash()
+    (csrc / "fa_fwd_kernel.h").write_text("// a comment\nint k() {\n  return 1;  /* same */\n}\n")
+    assert bench.kernel_source_hash() == h1
+    (csrc / "fa_fwd_kernel.h").write_text("int k() { return 2; }\n")
+    assert bench.kernel_source_hash() != h1
+
+
+def test_traffic_is_read_only_for_the_current_kernel(tmp_path, monkeypatch):
+    csrc = tmp_path / "exact_attention_17_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (csrc / "fa_fwd_kernel.h").write_text("int k() { return 1; }\n")
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h = bench.kernel_source_hash()
+    prof = tmp_path / "profiles" / "fa_fwd_full_traffic.txt"
+    prof.write_text("# header: ignored\nworkload: full\nkernel_source_hash: %s\nhbm_bytes_per_launch: 1234\n" % h)
+    assert bench.read_traffic("full") == 1234
+    assert bench.read_traffic("varlen") is None  # no such profile
+    prof.write_text("workload: full\nkernel_source_hash: 0000000000000000\nhbm_bytes_per_launch: 1234\n")
+    assert bench.read_traffic("full") is None  # taken on other kernel sources
+    prof.write_text("workload: gqa\nkernel_source_hash: %s\nhbm_bytes_per_launch: 1234\n" % h)
+    assert bench.read_traffic("full") is None  # another workload's numbers
+
+
+def test_committed_traffic_summaries_are_consistent():
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "fa_fwd_*_traffic.txt")))
+    assert paths
+    for p in paths:
+        vals = {}
+        with open(p) as f:
+            for line in f:
+                if line.startswith("#") or ":" not in line:
+                    continue
+                key, val = line.split(":", 1)
+                vals[key.strip()] = val.strip()
+        name = os.path.basename(p)[len("fa_fwd_"):-len("_traffic.txt")]
+        assert vals["workload"] == name
+        assert int(vals["hbm_bytes_per_launch"]) == int(vals["fetch_bytes_per_launch"]) + int(
+            vals["write_bytes_per_launch"])
+        assert len(vals["kernel_source_hash"]) == 16
