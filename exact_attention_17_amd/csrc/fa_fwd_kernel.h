@@ -633,8 +633,13 @@ fa_fwd_kernel(FaArgs a) {
   const int ght = lt / a.n_qtiles;
   const int gi = ght % a.group;
   const int hkb = ght / a.group;
-  const int b = hkb % a.batch;
-  const int hk = hkb / a.batch;  // the K/V head this query head reads
+  // Dense calls whose head rows are under 128 bytes (d_head 32) take the sequence outermost
+  // instead, so that the heads sharing a cache line of a token row are read by workgroups
+  // running at the same time (2.5 % on B64 N512 H16 d32, which fetches about twice its
+  // input bytes from HBM).
+  const bool seq_major = D * 2 < 128 && !a.cu_seqlens;
+  const int b = seq_major ? hkb / a.heads_kv : hkb % a.batch;
+  const int hk = seq_major ? hkb % a.heads_kv : hkb / a.batch;  // the K/V head this query head reads
   const int h = hk * a.group + gi;
 
   int nq, nk;
