@@ -190,6 +190,64 @@ def cpu_baseline(w, target_s=12.0):
                       % (n, "visible ones of" if causal else "all", nk, d, t)}
 
 
+def setup(name, dev, splits=0, which="fwd", atomic_dq=False):
+    """Inputs of a named workload resident on `dev`, output buffers, and the step the benchmark
+    times: one fa_fwd_ext call (or, for which="bwd", one fa_bwd call after one forward call).
+    The parity tests launch through this same function.  Returns a dict with w (the workload),
+    o, lse, step, cfg (the forward tile configuration), splits, flops, nbytes, stream and desc."""
+    import torch
+
+    from exact_attention_17_amd import fa, inputs, metrics
+
+    w = inputs.workload(name)
+    qd, kd, vd = w["q"].to(dev), w["k"].to(dev), w["v"].to(dev)
+    cu = w["cu_seqlens"].to(dev) if w["cu_seqlens"] is not None else None
+    o = torch.empty_like(qd)
+    lse = torch.empty((w["batch"], w["heads"], w["seqlen_q"]), dtype=torch.float32, device=dev)
+    causal, hkv = w["causal"], w["heads_kv"]
+    if cu is None:
+        flops = metrics.fwd_flops(w["batch"], w["heads"], w["seqlen_q"], w["seqlen_k"], w["d_head"], causal)
+        nbytes = metrics.fwd_bytes(w["batch"], w["heads"], w["seqlen_q"], w["seqlen_k"], w["d_head"],
+                                   heads_kv=hkv)
+    else:
+        flops = metrics.varlen_fwd_flops(w["lengths"], w["heads"], w["d_head"], causal)
+        nbytes = metrics.varlen_fwd_bytes(w["lengths"], w["heads"], w["d_head"], heads_kv=hkv)
+    dtype_code = fa.FA_FP16 if w["dtype"] == "fp16" else fa.FA_BF16
+    cfg = fa.fa_fwd_get_config_ext(w["batch"], w["seqlen_q"], w["seqlen_k"], w["heads"], w["d_head"], dtype_code,
+                                   varlen=cu is not None, causal=causal)
+    splits = splits if splits > 0 else fa.fa_fwd_choose_splits(
+        w["batch"], w["seqlen_q"], w["seqlen_k"], w["heads"], w["d_head"], dtype_code, causal, cu is not None)
+    workspace = None
+    if splits > 1:  # allocated before timing; the library allocates nothing
+        workspace = torch.empty(fa.fa_fwd_workspace_bytes(w["batch"], w["seqlen_q"], w["heads"], w["d_head"],
+                                                          splits), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.fa_fwd_ext(qd, kd, vd, o, lse, scale=w["scale"], causal=causal, cu_seqlens=cu,
+                      max_seqlen=w["max_seqlen"], num_splits=splits, workspace=workspace, stream=stream)
+
+    out = dict(w=w, o=o, lse=lse, step=step, cfg=cfg, splits=splits, flops=flops, nbytes=nbytes, stream=stream,
+               desc="fa_fwd_ext tiles %r, %d split(s)" % (cfg, splits))
+    if which == "bwd":
+        step()  # O and LSE of this workload
+        g = torch.Generator().manual_seed(int(w["seed"]) + 1000)
+        dout = torch.randn(tuple(qd.shape), generator=g, dtype=torch.float32).to(qd.dtype).to(dev)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        bws = torch.empty(fa.fa_bwd_workspace_bytes(w["batch"], w["seqlen_q"], w["heads"], w["d_head"],
+                                                    atomic_dq), dtype=torch.uint8, device=dev)
+        # algorithmic bytes: Q, K, V, O, dO read and dQ, dK, dV written (16-bit), LSE read and
+        # D, L log2(e) written once (fp32 per query row)
+        out["flops"] = flops * 5 // 2
+        out["nbytes"] = 2 * nbytes + 2 * 4 * qd.numel() // w["d_head"]
+
+        def bstep():
+            fa.fa_bwd(qd, kd, vd, o, lse, dout, dq, dk, dv, scale=w["scale"], causal=causal, cu_seqlens=cu,
+                      max_seqlen=w["max_seqlen"], atomic_dq=atomic_dq, workspace=bws, stream=stream)
+        out.update(step=bstep, dq=dq, dk=dk, dv=dv, desc="fa_bwd atomic_dq=%d" % int(bool(atomic_dq)))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,7 +271,7 @@ def main():
 
     import torch
 
-    from exact_attention_17_amd import fa, inputs, metrics
+    from exact_attention_17_amd import fa
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -225,49 +283,10 @@ def main():
 
     dev = torch.device("cuda:0")
     log("generating inputs for workload %s" % args.workload)
-    w = inputs.workload(args.workload)
-    qd, kd, vd = w["q"].to(dev), w["k"].to(dev), w["v"].to(dev)
-    cu = w["cu_seqlens"].to(dev) if w["cu_seqlens"] is not None else None
-    o = torch.empty_like(qd)
-    lse = torch.empty((w["batch"], w["heads"], w["seqlen_q"]), dtype=torch.float32, device=dev)
+    st = setup(args.workload, dev, splits=args.splits, which=args.which, atomic_dq=args.atomic_dq)
+    w, cfg, splits, flops, nbytes, step = st["w"], st["cfg"], st["splits"], st["flops"], st["nbytes"], st["step"]
+    stream = st["stream"]
     causal, hkv = w["causal"], w["heads_kv"]
-    if cu is None:
-        flops = metrics.fwd_flops(w["batch"], w["heads"], w["seqlen_q"], w["seqlen_k"], w["d_head"], causal)
-        nbytes = metrics.fwd_bytes(w["batch"], w["heads"], w["seqlen_q"], w["seqlen_k"], w["d_head"],
-                                   heads_kv=hkv)
-    else:
-        flops = metrics.varlen_fwd_flops(w["lengths"], w["heads"], w["d_head"], causal)
-        nbytes = metrics.varlen_fwd_bytes(w["lengths"], w["heads"], w["d_head"], heads_kv=hkv)
-    dtype_code = fa.FA_FP16 if w["dtype"] == "fp16" else fa.FA_BF16
-    cfg = fa.fa_fwd_get_config_ext(w["batch"], w["seqlen_q"], w["seqlen_k"], w["heads"], w["d_head"], dtype_code,
-                                   varlen=cu is not None, causal=causal)
-    splits = args.splits if args.splits > 0 else fa.fa_fwd_choose_splits(
-        w["batch"], w["seqlen_q"], w["seqlen_k"], w["heads"], w["d_head"], dtype_code, causal, cu is not None)
-    workspace = None
-    if splits > 1:  # allocated before timing; the library allocates nothing
-        workspace = torch.empty(fa.fa_fwd_workspace_bytes(w["batch"], w["seqlen_q"], w["heads"], w["d_head"],
-                                                          splits), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def step():
-        fa.fa_fwd_ext(qd, kd, vd, o, lse, scale=w["scale"], causal=causal, cu_seqlens=cu,
-                      max_seqlen=w["max_seqlen"], num_splits=splits, workspace=workspace, stream=stream)
-
-    if args.which == "bwd":
-        step()  # O and LSE of this workload
-        g = torch.Generator().manual_seed(int(w["seed"]) + 1000)
-        dout = torch.randn(tuple(qd.shape), generator=g, dtype=torch.float32).to(qd.dtype).to(dev)
-        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
-        bws = torch.empty(fa.fa_bwd_workspace_bytes(w["batch"], w["seqlen_q"], w["heads"], w["d_head"],
-                                                    args.atomic_dq), dtype=torch.uint8, device=dev)
-        flops = flops * 5 // 2
-        # algorithmic bytes: Q, K, V, O, dO read and dQ, dK, dV written (16-bit), LSE read and
-        # D, L log2(e) written once (fp32 per query row)
-        nbytes = 2 * nbytes + 2 * 4 * qd.numel() // w["d_head"]
-
-        def step():  # noqa: F811
-            fa.fa_bwd(qd, kd, vd, o, lse, dout, dq, dk, dv, scale=w["scale"], causal=causal, cu_seqlens=cu,
-                      max_seqlen=w["max_seqlen"], atomic_dq=args.atomic_dq, workspace=bws, stream=stream)
 
     for _ in range(args.warmup):
         step()

@@ -59,7 +59,7 @@ __global__ void __launch_bounds__(256) fa_bwd_pre_kernel(BwdArgs a) {
   int64_t qrow0;
   if (a.cu_seqlens) {
     qrow0 = a.cu_seqlens[b];
-    nq = a.cu_seqlens[b + 1] - a.cu_seqlens[b];
+    nq = min(a.cu_seqlens[b + 1] - a.cu_seqlens[b], a.seqlen_q);  // rows past max_seqlen: not used
   } else {
     nq = a.seqlen_q;
     qrow0 = (int64_t)b * nq;
@@ -118,7 +118,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(BwdArgs a) {
   int64_t qrow0;
   if (a.cu_seqlens) {
     qrow0 = a.cu_seqlens[b];
-    nq = a.cu_seqlens[b + 1] - a.cu_seqlens[b];
+    nq = min(a.cu_seqlens[b + 1] - a.cu_seqlens[b], a.seqlen_q);  // rows past max_seqlen: not used
   } else {
     nq = a.seqlen_q;
     qrow0 = (int64_t)b * nq;
@@ -261,7 +261,7 @@ fa_bwd_kernel(BwdArgs a) {
   int64_t qrow0, krow0;
   if (a.cu_seqlens) {
     const int s0 = a.cu_seqlens[b], s1 = a.cu_seqlens[b + 1];
-    nq = nk = s1 - s0;
+    nq = nk = min(s1 - s0, a.seqlen_q);  // tokens past max_seqlen (a broken contract): not used
     qrow0 = krow0 = s0;
   } else {
     nq = a.seqlen_q;
@@ -509,7 +509,7 @@ fa_bwd_dq_pass_kernel(BwdArgs a) {
   int64_t qrow0, krow0;
   if (a.cu_seqlens) {
     const int s0 = a.cu_seqlens[b], s1 = a.cu_seqlens[b + 1];
-    nq = nk = s1 - s0;
+    nq = nk = min(s1 - s0, a.seqlen_q);  // tokens past max_seqlen (a broken contract): not used
     qrow0 = krow0 = s0;
   } else {
     nq = a.seqlen_q;

@@ -645,8 +645,10 @@ fa_fwd_kernel(FaArgs a) {
   int nq, nk;
   int64_t qrow0, krow0;
   if (a.cu_seqlens) {
+    // a sequence longer than max_seqlen (the LSE row pitch) breaks the caller's contract;
+    // only its first max_seqlen tokens are used, so no access leaves the buffers
     const int s0 = a.cu_seqlens[b], s1 = a.cu_seqlens[b + 1];
-    nq = nk = s1 - s0;
+    nq = nk = min(s1 - s0, a.seqlen_q);
     qrow0 = krow0 = s0;
   } else {
     nq = a.seqlen_q;
@@ -779,12 +781,16 @@ fa_fwd_kernel(FaArgs a) {
       } else {
         // this wavefront's pieces of tile j landed: at most the later tiles' loads pending
         const int ahead = min(STAGES - 2, ntl - 1 - j);
-        if (ahead <= 0)
+        if (ahead <= 0) {
           wait_vmcnt<0>();
-        else if (STAGES < 4 || ahead == 1)
+        } else if constexpr (STAGES < 4) {
           wait_vmcnt<LPT>();
-        else
-          wait_vmcnt<2 * LPT>();
+        } else {
+          if (ahead == 1)
+            wait_vmcnt<LPT>();
+          else
+            wait_vmcnt<2 * LPT>();
+        }
       }
       wg_barrier();  // ... and everyone's; and everyone is done with tile j - 1
       if constexpr (STAGES >= 2) {

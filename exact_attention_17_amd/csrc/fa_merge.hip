@@ -31,7 +31,7 @@ __global__ void __launch_bounds__(256) fa_merge_kernel(MergeArgs a) {
   int64_t qrow0;
   if (a.cu_seqlens) {
     qrow0 = a.cu_seqlens[b];
-    nq = a.cu_seqlens[b + 1] - a.cu_seqlens[b];
+    nq = min(a.cu_seqlens[b + 1] - a.cu_seqlens[b], a.seqlen_q);  // rows past max_seqlen: not used
   } else {
     nq = a.seqlen_q;
     qrow0 = (int64_t)b * nq;

@@ -161,6 +161,23 @@ def _check_tensors(q, k, v, cu_seqlens):
         raise TypeError("cu_seqlens must be an int32 device tensor")
 
 
+def _outputs(q, o, lse, batch, heads, nq):
+    """Allocate o and lse, or check caller-supplied ones against what the kernels write: o a
+    contiguous device tensor shaped and typed like q, lse a contiguous float32 device tensor
+    [batch, n_heads, seqlen_q] (packed: max_seqlen rows per sequence)."""
+    import torch
+    if o is None:
+        o = torch.empty_like(q)
+    elif not o.is_cuda or o.device != q.device or not o.is_contiguous() or o.shape != q.shape or o.dtype != q.dtype:
+        raise ValueError("o must be a contiguous device tensor on q's device, shaped and typed like q")
+    if lse is None:
+        lse = torch.empty((batch, heads, nq), dtype=torch.float32, device=q.device)
+    elif not lse.is_cuda or lse.device != q.device or not lse.is_contiguous() or lse.dtype != torch.float32 or \
+            tuple(lse.shape) != (batch, heads, nq):
+        raise ValueError("lse must be a contiguous float32 device tensor [batch, n_heads, seqlen_q] on q's device")
+    return o, lse
+
+
 def fa_fwd(q, k, v, o=None, lse=None, scale=None, cu_seqlens=None, max_seqlen=None, stream=None):
     """Attention forward on torch device tensors; returns (o, lse).
 
@@ -169,15 +186,11 @@ def fa_fwd(q, k, v, o=None, lse=None, scale=None, cu_seqlens=None, max_seqlen=No
     o like q, lse [B, H, max_seqlen] (rows past a sequence's end untouched).
     o and lse may be given (preallocated); otherwise they are allocated with torch.
     """
-    import torch
     batch, nq, nk, heads, _, d = _shape_args(q, k, v, cu_seqlens, max_seqlen)
     _check_tensors(q, k, v, cu_seqlens)
     if scale is None:
         scale = d ** -0.5
-    if o is None:
-        o = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((batch, heads, nq), dtype=torch.float32, device=q.device)
+    o, lse = _outputs(q, o, lse, batch, heads, nq)
     st = lib().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), batch, nq,
                       nk, heads, d, float(scale), cu_seqlens.data_ptr() if cu_seqlens is not None else None,
                       _dtype_code(q), _stream_handle(stream, q.device))
@@ -199,10 +212,7 @@ def fa_fwd_ext(q, k, v, o=None, lse=None, scale=None, causal=False, cu_seqlens=N
     _check_tensors(q, k, v, cu_seqlens)
     if scale is None:
         scale = d ** -0.5
-    if o is None:
-        o = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((batch, heads, nq), dtype=torch.float32, device=q.device)
+    o, lse = _outputs(q, o, lse, batch, heads, nq)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         if not workspace.is_cuda:
@@ -242,6 +252,10 @@ def fa_bwd(q, k, v, o, lse, dout, dq=None, dk=None, dv=None, scale=None, causal=
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    for name, g, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if not g.is_cuda or g.device != q.device or not g.is_contiguous() or g.shape != like.shape or \
+                g.dtype != like.dtype:
+            raise ValueError("%s must be a contiguous device tensor shaped and typed like its input" % name)
     if workspace is None:
         workspace = torch.empty(fa_bwd_workspace_bytes(batch, nq, heads, d, atomic_dq), dtype=torch.uint8,
                                 device=q.device)

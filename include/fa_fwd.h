@@ -31,7 +31,10 @@
  *                   written only for i < its length, other rows untouched.
  *    The contents of cu_seqlens live on the device and are a precondition
  *    (not checked): they must describe sequences of length <= max_seqlen
- *    inside the q/k/v/o allocations.
+ *    inside the q/k/v/o allocations.  A sequence longer than max_seqlen
+ *    breaks that contract; the kernels then use only its first max_seqlen
+ *    tokens (its later O rows are not written), so LSE writes stay inside
+ *    [batch, n_heads, max_seqlen].
  *  - scale is the factor on the raw dot products (1/sqrt(d_head) is usual);
  *    it must be finite and > 0.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)

@@ -7,3 +7,4 @@ calls it.
 """
 from .oracle import (Oracle, attention, attention_bwd, attention_bwd_rows, attention_online,  # noqa: F401
                      attention_rows, build, compile_source, library_path, num_threads, source_text)
+from . import attn_matmul  # noqa: F401  (whole-matrix fp64 oracle for full-size checks)

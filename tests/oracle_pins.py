@@ -317,11 +317,6 @@ def pin_grouped_heads_are_repeated_heads(orc):
             o2, lse2 = orc.attention(q, krep, vrep, 0.5, causal=causal)
             np.testing.assert_allclose(o, o2, rtol=0, atol=1e-14)
             np.testing.assert_allclose(lse, lse2, rtol=0, atol=1e-14)
-            rows = [(0, heads - 1, 8), (1, 1, 3), (1, g % heads, 0)]
-            orow, lrow = orc.attention_rows(q, k, v, 0.5, rows, causal=causal)
-            for n, (b, h, i) in enumerate(rows):
-                np.testing.assert_allclose(orow[n], o[b, i, h], rtol=0, atol=1e-14)
-                assert abs(lrow[n] - lse[b, h, i]) < 1e-14
     lens = [4, 9]
     cu = np.concatenate([[0], np.cumsum(lens)])
     q = _rand(rng, 13, heads, 8)
@@ -330,6 +325,51 @@ def pin_grouped_heads_are_repeated_heads(orc):
     o2, lse2 = orc.attention(q, np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1), 0.5, cu_seqlens=cu)
     np.testing.assert_allclose(o, o2, rtol=0, atol=1e-14)
     np.testing.assert_allclose(lse, lse2, rtol=0, atol=1e-14, equal_nan=True)
+
+
+def pin_heads_are_independent(orc):
+    """Attention is defined per (batch, head): each head of a many-head call (dense and
+    packed, grouped K/V heads, plain and causal) equals a one-head call on that head's
+    Q and its K/V head alone."""
+    rng = np.random.default_rng(34)
+    heads = 7
+    for hkv in (7, 1):
+        g = heads // hkv
+        q = _rand(rng, 2, 10, heads, 8)
+        k, v = _rand(rng, 2, 12, hkv, 8), _rand(rng, 2, 12, hkv, 8)
+        for causal in (False, True):
+            o, lse = orc.attention(q, k, v, 0.5, causal=causal)
+            for h in range(heads):
+                sl = slice(h // g, h // g + 1)
+                oh, lseh = orc.attention(q[:, :, h:h + 1], k[:, :, sl], v[:, :, sl], 0.5, causal=causal)
+                np.testing.assert_allclose(o[:, :, h:h + 1], oh, rtol=0, atol=1e-14)
+                np.testing.assert_allclose(lse[:, h:h + 1], lseh, rtol=0, atol=1e-14)
+    lens = [3, 8]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v = _rand(rng, 11, heads, 8), _rand(rng, 11, heads, 8), _rand(rng, 11, heads, 8)
+    o, lse = orc.attention(q, k, v, 0.5, cu_seqlens=cu)
+    for h in range(heads):
+        oh, lseh = orc.attention(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], 0.5, cu_seqlens=cu)
+        np.testing.assert_allclose(o[:, h:h + 1], oh, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lse[:, h:h + 1], lseh, rtol=0, atol=1e-14, equal_nan=True)
+
+
+def pin_grouped_heads_rows_entry(orc):
+    """The selected-rows entry point agrees with the full one under grouped K/V heads
+    (MQA to groups of 2), plain and causal."""
+    rng = np.random.default_rng(33)
+    heads = 6
+    for hkv in (1, 3):
+        g = heads // hkv
+        q = _rand(rng, 2, 9, heads, 8)
+        k, v = _rand(rng, 2, 13, hkv, 8), _rand(rng, 2, 13, hkv, 8)
+        for causal in (False, True):
+            o, lse = orc.attention(q, k, v, 0.5, causal=causal)
+            rows = [(0, heads - 1, 8), (1, 1, 3), (1, g % heads, 0)]
+            orow, lrow = orc.attention_rows(q, k, v, 0.5, rows, causal=causal)
+            for n, (b, h, i) in enumerate(rows):
+                np.testing.assert_allclose(orow[n], o[b, i, h], rtol=0, atol=1e-14)
+                assert abs(lrow[n] - lse[b, h, i]) < 1e-14
 
 
 def _loss(orc, q, k, v, dout, scale, **kw):
@@ -450,5 +490,15 @@ PINS = [pin_hand_2x2, pin_hand_4x4, pin_values_one, pin_identical_keys, pin_domi
         pin_varlen_is_per_sequence, pin_rows_match_full, pin_causal_hand_3x3,
         pin_causal_identical_keys, pin_causal_value_identity, pin_causal_is_prefix_attention,
         pin_causal_block_skipping_is_exact, pin_causal_varlen_is_per_sequence,
-        pin_grouped_heads_are_repeated_heads, pin_bwd_finite_differences, pin_bwd_tiny_all_coordinates,
+        pin_grouped_heads_are_repeated_heads, pin_heads_are_independent, pin_grouped_heads_rows_entry,
+        pin_bwd_finite_differences, pin_bwd_tiny_all_coordinates,
         pin_bwd_value_identities, pin_bwd_identical_keys_and_single_key, pin_bwd_rows_match_full]
+
+# Pins that need only the forward definition (orc.attention): the whole-matrix oracle is
+# held to these as well.
+FORWARD_PINS = [pin_hand_2x2, pin_hand_4x4, pin_values_one, pin_identical_keys, pin_dominant_logit,
+                pin_value_identity_is_softmax, pin_single_key, pin_permutations_and_linearity,
+                pin_shift_invariance, pin_large_logits, pin_varlen_is_per_sequence, pin_causal_hand_3x3,
+                pin_causal_identical_keys, pin_causal_value_identity, pin_causal_is_prefix_attention,
+                pin_causal_varlen_is_per_sequence, pin_grouped_heads_are_repeated_heads,
+                pin_heads_are_independent]

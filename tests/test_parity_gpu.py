@@ -38,12 +38,13 @@ def run_gpu(q, k, v, scale, cu=None, max_seqlen=None, lse_fill=None):
     dev = torch.device("cuda:0")
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     cud = cu.to(dev) if cu is not None else None
-    lse = None
-    if lse_fill is not None:
-        batch = cu.numel() - 1 if cu is not None else q.shape[0]
-        nq = max_seqlen if cu is not None else q.shape[1]
-        lse = torch.full((batch, q.shape[-2], nq), lse_fill, dtype=torch.float32, device=dev)
-    o, lse = fa.fa_fwd(qd, kd, vd, lse=lse, scale=scale, cu_seqlens=cud, max_seqlen=max_seqlen)
+    # O and LSE start as NaN, so an element no workgroup wrote cannot pass as a result
+    batch = cu.numel() - 1 if cu is not None else q.shape[0]
+    nq = max_seqlen if cu is not None else q.shape[1]
+    lse = torch.full((batch, q.shape[-2], nq), float("nan") if lse_fill is None else lse_fill,
+                     dtype=torch.float32, device=dev)
+    o = torch.full_like(qd, float("nan"))
+    o, lse = fa.fa_fwd(qd, kd, vd, o=o, lse=lse, scale=scale, cu_seqlens=cud, max_seqlen=max_seqlen)
     torch.cuda.synchronize()
     return o.cpu().to(torch.float64).numpy(), lse.cpu().to(torch.float64).numpy()
 
