@@ -4,7 +4,9 @@
 
 A step is one fa_fwd call over the whole batch of the full workload
 (B16 N4096 H16 d128 bf16, non-causal, seeded N(0,1) inputs resident in HBM before
-timing).  Prints ONE JSON line with the throughput in TFLOP/s
+timing; the tile configuration is the one the library's autotuner picks on those buffers
+before timing -- every compiled configuration timed in interleaved rounds -- or, with
+--no-tune, the built-in choice).  Prints ONE JSON line with the throughput in TFLOP/s
 (4 * B * H * Nq * Nk * d per step), the roofline figures of the kernel and the
 fp64 oracle timed on a bounded sample on the host cores.
 
@@ -190,11 +192,14 @@ def cpu_baseline(w, target_s=12.0):
                       % (n, "visible ones of" if causal else "all", nk, d, t)}
 
 
-def setup(name, dev, splits=0, which="fwd", atomic_dq=False):
+def setup(name, dev, splits=0, which="fwd", atomic_dq=False, tune=True, tune_rounds=5):
     """Inputs of a named workload resident on `dev`, output buffers, and the step the benchmark
     times: one fa_fwd_ext call (or, for which="bwd", one fa_bwd call after one forward call).
+    With tune, the library's autotuner first times every compiled tile configuration on these
+    buffers (fa_fwd_autotune_ext, interleaved median timing) and the step then runs its pick.
     The parity tests launch through this same function.  Returns a dict with w (the workload),
-    o, lse, step, cfg (the forward tile configuration), splits, flops, nbytes, stream and desc."""
+    o, lse, step, cfg (the forward tile configuration), splits, tuned (the tuner's report or
+    None), flops, nbytes, stream and desc."""
     import torch
 
     from exact_attention_17_amd import fa, inputs, metrics
@@ -213,22 +218,41 @@ def setup(name, dev, splits=0, which="fwd", atomic_dq=False):
         flops = metrics.varlen_fwd_flops(w["lengths"], w["heads"], w["d_head"], causal)
         nbytes = metrics.varlen_fwd_bytes(w["lengths"], w["heads"], w["d_head"], heads_kv=hkv)
     dtype_code = fa.FA_FP16 if w["dtype"] == "fp16" else fa.FA_BF16
-    cfg = fa.fa_fwd_get_config_ext(w["batch"], w["seqlen_q"], w["seqlen_k"], w["heads"], w["d_head"], dtype_code,
-                                   varlen=cu is not None, causal=causal)
-    splits = splits if splits > 0 else fa.fa_fwd_choose_splits(
-        w["batch"], w["seqlen_q"], w["seqlen_k"], w["heads"], w["d_head"], dtype_code, causal, cu is not None)
-    workspace = None
-    if splits > 1:  # allocated before timing; the library allocates nothing
-        workspace = torch.empty(fa.fa_fwd_workspace_bytes(w["batch"], w["seqlen_q"], w["heads"], w["d_head"],
-                                                          splits), dtype=torch.uint8, device=dev)
+    shape = (w["batch"], w["seqlen_q"], w["seqlen_k"], w["heads"], w["d_head"])
     stream = torch.cuda.current_stream(dev)
+    # Split workspace, allocated before timing (the library allocates nothing).  With the
+    # automatic count (splits = 0) every tile configuration may pick its own: room for the
+    # largest count, within 256 MiB (the library lowers a count to what the workspace holds).
+    want = splits if splits > 0 else fa.FA_MAX_SPLITS
+    ws_bytes = fa.fa_fwd_workspace_bytes(w["batch"], w["seqlen_q"], w["heads"], w["d_head"], want)
+    ws_bytes = min(ws_bytes, 256 << 20) // 16 * 16
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    tuned = None
+    if tune and which == "fwd":
+        chosen, ms = fa.fa_fwd_autotune_ext(qd, kd, vd, o, lse, scale=w["scale"], causal=causal, cu_seqlens=cu,
+                                            max_seqlen=w["max_seqlen"], num_splits=splits, workspace=workspace,
+                                            rounds=tune_rounds, stream=stream)
+        ranking = fa.fa_fwd_tune_ranking()
+        tuned = {"tuned": True, "candidates": len(ranking), "rounds": tune_rounds, "median_ms": round(ms, 5),
+                 "runner_up": {"tile": list(ranking[1][0].as_tuple()), "median_ms": round(ranking[1][1], 5)}
+                 if len(ranking) > 1 else None}
+    cfg, auto_splits, source = fa.fa_fwd_query_config(*shape, dtype_code, n_heads_kv=hkv, varlen=cu is not None,
+                                                      causal=causal)
+    if splits == 0:  # the count fa_fwd_ext will use: the automatic one, lowered to the workspace
+        splits = auto_splits
+        while splits > 1 and fa.fa_fwd_workspace_bytes(w["batch"], w["seqlen_q"], w["heads"], w["d_head"],
+                                                       splits) > ws_bytes:
+            splits -= 1
+        req_splits = 0
+    else:
+        req_splits = splits
 
     def step():
         fa.fa_fwd_ext(qd, kd, vd, o, lse, scale=w["scale"], causal=causal, cu_seqlens=cu,
-                      max_seqlen=w["max_seqlen"], num_splits=splits, workspace=workspace, stream=stream)
+                      max_seqlen=w["max_seqlen"], num_splits=req_splits, workspace=workspace, stream=stream)
 
-    out = dict(w=w, o=o, lse=lse, step=step, cfg=cfg, splits=splits, flops=flops, nbytes=nbytes, stream=stream,
-               desc="fa_fwd_ext tiles %r, %d split(s)" % (cfg, splits))
+    out = dict(w=w, o=o, lse=lse, step=step, cfg=cfg, splits=splits, tuned=tuned, flops=flops, nbytes=nbytes,
+               stream=stream, desc="fa_fwd_ext tiles %r (%s), %d split(s)" % (cfg, source, splits))
     if which == "bwd":
         step()  # O and LSE of this workload
         g = torch.Generator().manual_seed(int(w["seed"]) + 1000)
@@ -261,6 +285,8 @@ def main():
     ap.add_argument("--atomic-dq", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tune", action="store_true", help="time the built-in tile choice, without tuning")
+    ap.add_argument("--tune-rounds", type=int, default=5)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -283,7 +309,11 @@ def main():
 
     dev = torch.device("cuda:0")
     log("generating inputs for workload %s" % args.workload)
-    st = setup(args.workload, dev, splits=args.splits, which=args.which, atomic_dq=args.atomic_dq)
+    st = setup(args.workload, dev, splits=args.splits, which=args.which, atomic_dq=args.atomic_dq,
+               tune=not args.no_tune, tune_rounds=args.tune_rounds)
+    if st["tuned"]:
+        log("tuned over %d configurations: %r, median %.4f ms" % (st["tuned"]["candidates"], st["cfg"],
+                                                                 st["tuned"]["median_ms"]))
     w, cfg, splits, flops, nbytes, step = st["w"], st["cfg"], st["splits"], st["flops"], st["nbytes"], st["step"]
     stream = st["stream"]
     causal, hkv = w["causal"], w["heads_kv"]
@@ -335,7 +365,7 @@ def main():
         "config": {"workload": wl, "batch": w["batch"], "seq_len_q": w["seqlen_q"], "seq_len_k": w["seqlen_k"],
                    "heads": w["heads"], "heads_kv": hkv, "d_head": w["d_head"], "causal": causal,
                    "tile": ({"br": cfg.br, "bc": cfg.bc, "waves": cfg.waves, "stages": cfg.stages,
-                             "schedule": cfg.schedule} if args.which == "fwd" else
+                             "schedule": cfg.schedule, "tuned": bool(st["tuned"])} if args.which == "fwd" else
                             {"dkdv_keys_per_workgroup": 64 if w["d_head"] == 32 else 128,
                              "dq_pass_rows_per_workgroup": 256 if w["d_head"] == 128 else 128}),
                    "num_splits": splits, "pass": args.which,
@@ -346,6 +376,7 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": nbytes,
                      "algorithmic_flops": flops},
         "cpu_baseline": cpu,
+        "tuning": st["tuned"],
         "launch_ms": {"median": round(per_launch[len(per_launch) // 2], 5), "min": round(per_launch[0], 5)},
         "device_peak": device_peak(),
     }

@@ -23,13 +23,36 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Werr
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+INST = "fa_fwd_inst.hip"  # compiled once per (d_head, dtype, part of the configuration space)
+SPACE_PARTS = 4           # kSpaceParts in csrc/fa_internal.h
+
+
+def units():
+    """(source, object name, extra defines) for every compile unit."""
+    out = []
+    for f in sorted(os.listdir(CSRC)):
+        if not f.endswith((".hip", ".cpp")):
+            continue
+        src = os.path.join(CSRC, f)
+        if f == INST:
+            for d in (32, 64, 128):
+                for f16 in (0, 1):
+                    for part in range(SPACE_PARTS):
+                        out.append((src, "fa_fwd_inst_d%d_%s_p%d.o" % (d, "fp16" if f16 else "bf16", part),
+                                    ["-DFA_INST_D=%d" % d, "-DFA_INST_F16=%d" % f16, "-DFA_INST_PART=%d" % part]))
+        else:
+            out.append((src, f + ".o", []))
+    return out
+
+
 def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
+    return sorted({u[0] for u in units()})
 
 
-def _compile(src, extra):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + extra + ["-c", src, "-o", obj]
+def _compile(unit, extra):
+    src, objname, defines = unit
+    obj = os.path.join(BUILD, objname)
+    cmd = [HIPCC] + FLAGS + defines + extra + ["-c", src, "-o", obj]
     p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(ln for ln in p.stdout.splitlines() if "is not a recognized feature" not in ln)
     if p.returncode != 0:
@@ -42,7 +65,9 @@ def build(jobs=None, extra=(), verbose=False):
     os.makedirs(BUILD, exist_ok=True)
     jobs = jobs or min(8, os.cpu_count() or 4)
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        results = list(ex.map(lambda s: _compile(s, list(extra)), sources()))
+        # longest units first (the instantiation parts), so the pool drains evenly
+        todo = sorted(units(), key=lambda u: u[0].endswith(INST), reverse=True)
+        results = list(ex.map(lambda u: _compile(u, list(extra)), todo))
     if verbose:
         for obj, out in results:
             if out.strip():

@@ -7,17 +7,25 @@
 //     dQ = scale dS K,   dK = scale dS^T Q,
 // in the order of that page's blocked backward (section 13.2) and FlashAttention-2's
 // parallelisation (section 14.2): one workgroup per (batch, K/V head, tile of BKV keys)
-// keeps its keys' dK and dV in registers over the whole loop on query tiles, and adds its
-// share of dQ into an fp32 accumulator in HBM with atomic adds.  With grouped K/V heads the
-// loop also runs over every query head of the group, so dK and dV of a K/V head are summed
-// on chip (section 14.2).  Under the causal mask the loop starts at the first query tile
-// that can see the workgroup's first key, and only tiles crossing the diagonal are masked.
+// keeps its keys' dK and dV in registers over the whole loop on query tiles.  With grouped
+// K/V heads the loop also runs over every query head of the group, so dK and dV of a K/V
+// head are summed on chip (section 14.2).  Under the causal mask the loop starts at the
+// first query tile that can see the workgroup's first key, and only tiles crossing the
+// diagonal are masked.
 //
-// Three kernels:
-//   fa_bwd_pre_kernel   D_i = <dO_i, O_i> (the page's simplification of P_i . dP_i),
-//                       L_i log2(e) for exp2, and a zeroed dQ accumulator row;
-//   fa_bwd_kernel       the main loop;
-//   fa_bwd_dq_kernel    dQ = 16-bit(scale x accumulator).
+// dQ is formed one of two ways:
+//  * by default, a second, query-parallel pass (fa_bwd_dq_pass_kernel): one workgroup per
+//    (batch, head, query tile) recomputes S, P, dP and dS over the key tiles and sums
+//    dQ = scale dS K on chip, storing it once (no atomics; bitwise repeatable);
+//  * with atomic_dq (the page's Algorithm 2), the dK/dV kernel adds each workgroup's share
+//    of dQ into an fp32 accumulator in HBM with atomic adds, converted at the end.
+//
+// Kernels:
+//   fa_bwd_pre_kernel      D_i = <dO_i, O_i> (the page's simplification of P_i . dP_i),
+//                          L_i log2(e) for exp2, and (atomic_dq) a zeroed dQ accumulator row;
+//   fa_bwd_kernel          the dK/dV loop (and, with atomic_dq, the atomic dQ adds);
+//   fa_bwd_dq_pass_kernel  the default dQ pass;
+//   fa_bwd_dq_kernel       (atomic_dq) dQ = 16-bit(scale x accumulator).
 //
 // gfx950 mapping (the forward's building blocks in other roles):
 //  * Each wavefront owns 32 keys.  S = Q K^T and dP = dO V^T are formed with the K and V
@@ -28,10 +36,13 @@
 //    dV^T += dO^T P and dK^T += Q^T dS, whose A operands are read transposed from the
 //    row-major dO and Q tiles with ds_read_b64_tr_b16 (the forward's pv_block, with query
 //    rows in place of key rows).
-//  * dS also goes to LDS as dS^T [key][query]; after a barrier each wavefront forms two
-//    32x32 tiles of dQ = dS K over all the workgroup's keys, both operands read transposed
-//    (dS^T and the resident K tile), and adds them to the accumulator with global atomic
-//    adds (no return value).
+//  * atomic_dq: dS also goes to LDS as dS^T [key][query]; after a barrier each wavefront
+//    forms two 32x32 tiles of dQ = dS K over all the workgroup's keys, both operands read
+//    transposed (dS^T and the resident K tile), and adds them to the accumulator with
+//    global atomic adds (no return value).
+//  * The dQ pass is the forward's structure with a third product: S^T = K Q^T and
+//    dP^T = V dO^T with K, V tiles in LDS and Q, dO in registers, then dQ^T += K^T dS^T
+//    with K read transposed.
 //  * Q, dO, L log2(e) and D of the next query tile stream into LDS (buffer_load ... lds)
 //    while the current one is used.
 #pragma once

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -44,16 +45,24 @@ std::vector<KernelEntry> *g_entries = nullptr;
 
 void add_entry(const KernelEntry &e) { g_entries->push_back(e); }
 
+template <int D, bool F16, int P = 0>
+void register_all() {
+  if constexpr (P < fa::kSpaceParts) {
+    fa::register_part<D, F16, P>(add_entry);
+    register_all<D, F16, P + 1>();
+  }
+}
+
 const std::vector<KernelEntry> &entries() {
   static std::once_flag once;
   std::call_once(once, [] {
     g_entries = new std::vector<KernelEntry>();
-    fa::register_bf16_d32(add_entry);
-    fa::register_bf16_d64(add_entry);
-    fa::register_bf16_d128(add_entry);
-    fa::register_fp16_d32(add_entry);
-    fa::register_fp16_d64(add_entry);
-    fa::register_fp16_d128(add_entry);
+    register_all<32, false>();
+    register_all<64, false>();
+    register_all<128, false>();
+    register_all<32, true>();
+    register_all<64, true>();
+    register_all<128, true>();
   });
   return *g_entries;
 }
@@ -74,14 +83,32 @@ bool valid_d(int d) { return d == 32 || d == 64 || d == 128; }
 // ------------------------------------------------------ configuration choice
 std::mutex g_cfg_mu;
 std::map<std::pair<int, int>, fa_tile_config_t> g_forced;  // (d, dtype) -> config
-// (d, dtype, varlen, causal, ceil(log2(seqlen_q))) -> tuned config
-std::map<std::tuple<int, int, int, int, int>, fa_tile_config_t> g_tuned;
 
-int log2_bucket(int n) {
+// What a call's configuration choice depends on.
+struct Shape {
+  int batch, seqlen_q, seqlen_k, n_heads, n_heads_kv, d, dtype;
+  bool varlen, causal;
+};
+
+int log2_bucket(int64_t n) {
   int b = 0;
-  while ((1LL << b) < n) ++b;
+  while ((int64_t(1) << b) < n) ++b;
   return b;
 }
+
+// A tuned choice serves calls of the same kind and about the same size: (d_head, dtype,
+// varlen, causal, ceil(log2 of the query heads per K/V head), ceil(log2 seqlen_q),
+// ceil(log2 batch x n_heads)).
+typedef std::array<int, 7> TuneKey;
+TuneKey key_of(const Shape &s) {
+  return TuneKey{s.d, s.dtype, s.varlen ? 1 : 0, s.causal ? 1 : 0, log2_bucket(s.n_heads / s.n_heads_kv),
+                 log2_bucket(s.seqlen_q), log2_bucket((int64_t)s.batch * s.n_heads)};
+}
+struct Tuned {
+  fa_tile_config_t cfg;
+  float ms;  // the winner's median time per launch when it was tuned
+};
+std::map<TuneKey, Tuned> g_tuned;
 
 // Built-in choice, from sweeps of the compiled configurations on MI355X: a short query
 // tile gains nothing from more wavefronts; at d_head 128 and longer sequences eight
@@ -116,15 +143,99 @@ const fa_tile_config_t *env_config() {
   return have ? &cfg : nullptr;
 }
 
-fa_tile_config_t choose_config(int seqlen_q, int d, int dtype, bool varlen, bool causal) {
+// ------------------------------------------------------------ tuned-choice cache file
+// One line per tuned choice:
+//   d_head dtype varlen causal log2_group log2_seqlen_q log2_batch_heads : br bc waves stages schedule ms
+// Lines starting with '#', malformed lines and configurations this build does not have are
+// skipped on reading.
+const char *kCacheHeader =
+    "# fa_fwd tuned tile configurations: d_head dtype varlen causal log2_group log2_seqlen_q "
+    "log2_batch_heads : br bc waves stages schedule ms";
+
+// Caller holds g_cfg_mu.  Returns the number of entries taken, or -1 if the file cannot be read.
+int load_cache_locked(const char *path) {
+  FILE *f = std::fopen(path, "r");
+  if (!f) return -1;
+  char line[512];
+  int n = 0;
+  while (std::fgets(line, sizeof line, f)) {
+    if (line[0] == '#') continue;
+    TuneKey k;
+    fa_tile_config_t c;
+    float ms = 0.f;
+    if (std::sscanf(line, "%d %d %d %d %d %d %d : %d %d %d %d %d %f", &k[0], &k[1], &k[2], &k[3], &k[4], &k[5],
+                    &k[6], &c.br, &c.bc, &c.waves, &c.stages, &c.schedule, &ms) != 13)
+      continue;
+    if (!find_entry(k[1], k[0], c)) continue;
+    g_tuned[k] = Tuned{c, ms};
+    ++n;
+  }
+  std::fclose(f);
+  return n;
+}
+
+// Caller holds g_cfg_mu.  Writes the whole table (through a temporary file, renamed into place).
+int save_cache_locked(const char *path) {
+  const std::string tmp = std::string(path) + ".tmp";
+  FILE *f = std::fopen(tmp.c_str(), "w");
+  if (!f) return -1;
+  std::fprintf(f, "%s\n", kCacheHeader);
+  for (const auto &kv : g_tuned) {
+    const TuneKey &k = kv.first;
+    const fa_tile_config_t &c = kv.second.cfg;
+    std::fprintf(f, "%d %d %d %d %d %d %d : %d %d %d %d %d %.5f\n", k[0], k[1], k[2], k[3], k[4], k[5], k[6], c.br,
+                 c.bc, c.waves, c.stages, c.schedule, kv.second.ms);
+  }
+  const bool good = std::fclose(f) == 0;
+  if (!good || std::rename(tmp.c_str(), path) != 0) {
+    std::remove(tmp.c_str());
+    return -1;
+  }
+  return 0;
+}
+
+// FA_FWD_TUNE_CACHE names a cache file: read at the first configuration lookup, rewritten
+// after each tuning.
+const char *cache_path() {
+  const char *p = std::getenv("FA_FWD_TUNE_CACHE");
+  return (p && *p) ? p : nullptr;
+}
+
+void load_env_cache_once() {
+  static std::once_flag once;
+  std::call_once(once, [] {
+    if (const char *p = cache_path()) {
+      std::lock_guard<std::mutex> lk(g_cfg_mu);
+      (void)load_cache_locked(p);
+    }
+  });
+}
+
+// Where a configuration choice came from (fa_fwd_query_config's source).
+enum { kSrcDefault = 0, kSrcTuned = 1, kSrcEnv = 2, kSrcForced = 3 };
+
+fa_tile_config_t choose_config(const Shape &s, int *source = nullptr) {
+  load_env_cache_once();
   const fa_tile_config_t *env = env_config();
   std::lock_guard<std::mutex> lk(g_cfg_mu);
-  auto f = g_forced.find({d, dtype});
-  if (f != g_forced.end()) return f->second;
-  if (env && find_entry(dtype, d, *env)) return *env;
-  auto t = g_tuned.find({d, dtype, varlen ? 1 : 0, causal ? 1 : 0, log2_bucket(seqlen_q)});
-  if (t != g_tuned.end()) return t->second;
-  return default_config(seqlen_q, d, causal);
+  int src = kSrcDefault;
+  fa_tile_config_t c;
+  auto f = g_forced.find({s.d, s.dtype});
+  auto t = g_tuned.find(key_of(s));
+  if (f != g_forced.end()) {
+    c = f->second;
+    src = kSrcForced;
+  } else if (env && find_entry(s.dtype, s.d, *env)) {
+    c = *env;
+    src = kSrcEnv;
+  } else if (t != g_tuned.end()) {
+    c = t->second.cfg;
+    src = kSrcTuned;
+  } else {
+    c = default_config(s.seqlen_q, s.d, s.causal);
+  }
+  if (source) *source = src;
+  return c;
 }
 
 // ------------------------------------------------------------ arg checks
@@ -246,21 +357,26 @@ Call make_call(const void *q, const void *k, const void *v, void *o, float *lse,
 
 constexpr int kNumCUs = 256;
 
-// Splits for about two workgroups per CU when the grid alone is smaller than the CU count;
-// each split keeps at least four key tiles (measured on MI355X over a few query rows
-// against 2K-32K keys: fewer tiles per split cost more in partial stores and merging than
-// the extra parallelism gains).
-int choose_splits(int batch, int seqlen_q, int seqlen_k, int n_heads, int d_head, int dtype, bool causal,
-                  bool varlen) {
-  const fa_tile_config_t c = choose_config(seqlen_q, d_head, dtype, varlen, causal);
-  const int64_t wgs = (int64_t)batch * n_heads * ((seqlen_q + c.br - 1) / c.br);
+// Splits for about two workgroups per CU when configuration c's grid alone is smaller than
+// the CU count; each split keeps at least four key tiles (measured on MI355X over a few query
+// rows against 2K-32K keys: fewer tiles per split cost more in partial stores and merging
+// than the extra parallelism gains).
+int splits_for(const fa_tile_config_t &c, const Shape &s) {
+  const int64_t wgs = (int64_t)s.batch * s.n_heads * ((s.seqlen_q + c.br - 1) / c.br);
   if (wgs >= kNumCUs) return 1;
-  const int64_t keys = causal ? std::min(seqlen_k, seqlen_q) : seqlen_k;
+  const int64_t keys = s.causal ? std::min(s.seqlen_k, s.seqlen_q) : s.seqlen_k;
   const int64_t nkt = (keys + c.bc - 1) / c.bc;
-  int64_t s = (2 * kNumCUs + wgs - 1) / wgs;
-  s = std::min<int64_t>(s, nkt / 4);
-  s = std::min<int64_t>(s, FA_MAX_SPLITS);
-  return (int)std::max<int64_t>(s, 1);
+  int64_t n = (2 * kNumCUs + wgs - 1) / wgs;
+  n = std::min<int64_t>(n, nkt / 4);
+  n = std::min<int64_t>(n, FA_MAX_SPLITS);
+  return (int)std::max<int64_t>(n, 1);
+}
+
+// The automatic count for c, lowered to the largest one whose partials fit the workspace.
+int splits_within(const fa_tile_config_t &c, const Shape &s, const void *workspace, size_t workspace_bytes) {
+  int n = splits_for(c, s);
+  while (n > 1 && (!workspace || workspace_bytes_of(s.batch, s.seqlen_q, s.n_heads, s.d, n) > workspace_bytes)) --n;
+  return n;
 }
 
 constexpr int kLdsLimit = 160 * 1024;
@@ -278,7 +394,157 @@ size_t bwd_bytes(int batch, int seqlen_q, int n_heads, int d_head, int atomic_dq
   return (size_t)batch * (size_t)seqlen_q * (size_t)n_heads * (size_t)((atomic_dq ? d_head : 0) + 2) * 4u;
 }
 
+// ------------------------------------------------------------ autotuner
+// Page "Flash Attention 2 Chapter6", Kernel 7: enumerate the configuration space, filter
+// what cannot run (LDS, spills), time the rest on the caller's buffers, keep the best.
+// Timing is made fair to every candidate: the clock is first brought to its loaded state
+// (a sequential sweep that starts cold favours whatever runs last: 12-20 % errors were seen
+// on MI355X), then all candidates are timed in interleaved rounds with a rotating order and
+// scored by their median, and the two best are timed against each other once more.
+constexpr int kMaxTuneRounds = 100;
+constexpr float kWarmMs = 40.f;    // GPU time spent warming up before any measurement
+constexpr float kSampleMs = 0.5f;  // launches per measurement: enough for about this long
+
+std::mutex g_tune_mu;  // one tuning at a time; guards g_last_ranking
+struct Candidate {
+  const KernelEntry *e = nullptr;
+  int splits = 1;
+  float ms = 0.f;  // median time per launch
+};
+struct Ranked {
+  fa_tile_config_t cfg;
+  float ms;
+};
+std::vector<Ranked> g_last_ranking;  // the last tuning's candidates, fastest first
+
+float median_of(std::vector<float> v) {
+  std::sort(v.begin(), v.end());
+  const size_t n = v.size();
+  return n % 2 ? v[n / 2] : 0.5f * (v[n / 2 - 1] + v[n / 2]);
+}
+
+// Owns a set of HIP events.
+struct Events {
+  std::vector<hipEvent_t> ev;
+  ~Events() {
+    for (hipEvent_t e : ev)
+      if (e) (void)hipEventDestroy(e);
+  }
+  int create(size_t n) {
+    ev.assign(n, nullptr);
+    for (auto &e : ev) {
+      hipError_t err = hipEventCreate(&e);
+      if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("hipEventCreate: ") + hipGetErrorString(err));
+    }
+    return FA_OK;
+  }
+};
+
+int hip_status(hipError_t err, const char *what) {
+  return err == hipSuccess ? FA_OK : fail(FA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(err));
+}
+
+// ms between two recorded events (the second already complete).
+int elapsed(hipEvent_t a, hipEvent_t b, float *ms) { return hip_status(hipEventElapsedTime(ms, a, b), "hipEventElapsedTime"); }
+
+int tune(const Call &call, const Shape &shape, int num_splits, void *workspace, size_t workspace_bytes, int rounds,
+         Candidate *best) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(call.stream);
+  std::vector<Candidate> cand;
+  const fa_tile_config_t dflt = default_config(shape.seqlen_q, shape.d, shape.causal);
+  size_t first = 0;
+  for (const auto &e : entries()) {
+    if (e.dtype != shape.dtype || e.d_head != shape.d) continue;
+    const fa_tile_config_t c = cfg_of(e);
+    if (lds_bytes_of(shape.d, c) > kLdsLimit) continue;  // does not fit one CU's LDS
+    hipFuncAttributes attr;
+    int st = hip_status(hipFuncGetAttributes(&attr, e.kernel), "hipFuncGetAttributes");
+    if (st != FA_OK) return st;
+    if (attr.localSizeBytes > 0) continue;  // spills registers
+    Candidate cd;
+    cd.e = &e;
+    cd.splits = num_splits == 0 ? splits_within(c, shape, workspace, workspace_bytes) : num_splits;
+    if (std::memcmp(&c, &dflt, sizeof c) == 0) first = cand.size();
+    cand.push_back(cd);
+  }
+  if (cand.empty()) return fail(FA_ERR_UNSUPPORTED, "no compiled configuration passed the LDS / spill filter");
+  const size_t n = cand.size();
+  auto launch = [&](const Candidate &c) { return launch_entry(*c.e, call, c.splits, workspace); };
+  Events evs;
+  int st = evs.create(n + 1);
+  if (st != FA_OK) return st;
+  auto &ev = evs.ev;
+  // Warm up on the built-in default: one timed launch sizes the warm-up and the samples.
+  if ((st = hip_status(hipEventRecord(ev[0], s), "hipEventRecord")) != FA_OK) return st;
+  if ((st = launch(cand[first])) != FA_OK) return st;
+  if ((st = hip_status(hipEventRecord(ev[1], s), "hipEventRecord")) != FA_OK) return st;
+  if ((st = hip_status(hipEventSynchronize(ev[1]), "hipEventSynchronize")) != FA_OK) return st;
+  float t1 = 0.f;
+  if ((st = elapsed(ev[0], ev[1], &t1)) != FA_OK) return st;
+  t1 = std::max(t1, 1e-3f);
+  const int warm = (int)std::min(4000.f, std::ceil(kWarmMs / t1));
+  const int reps = (int)std::min(256.f, std::max(1.f, std::ceil(kSampleMs / t1)));
+  for (int i = 0; i < warm; ++i)
+    if ((st = launch(cand[first])) != FA_OK) return st;
+  for (const auto &c : cand)  // every candidate once, untimed (first-launch costs)
+    if ((st = launch(c)) != FA_OK) return st;
+  // Interleaved rounds: round r times candidate (i + r) % n in position i.
+  std::vector<std::vector<float>> t(n);
+  for (int r = 0; r < rounds; ++r) {
+    if ((st = hip_status(hipEventRecord(ev[0], s), "hipEventRecord")) != FA_OK) return st;
+    for (size_t i = 0; i < n; ++i) {
+      for (int k = 0; k < reps; ++k)
+        if ((st = launch(cand[(i + r) % n])) != FA_OK) return st;
+      if ((st = hip_status(hipEventRecord(ev[i + 1], s), "hipEventRecord")) != FA_OK) return st;
+    }
+    if ((st = hip_status(hipEventSynchronize(ev[n]), "hipEventSynchronize")) != FA_OK) return st;
+    for (size_t i = 0; i < n; ++i) {
+      float ms = 0.f;
+      if ((st = elapsed(ev[i], ev[i + 1], &ms)) != FA_OK) return st;
+      t[(i + r) % n].push_back(ms / reps);
+    }
+  }
+  for (size_t i = 0; i < n; ++i) cand[i].ms = median_of(t[i]);
+  std::stable_sort(cand.begin(), cand.end(), [](const Candidate &a, const Candidate &b) { return a.ms < b.ms; });
+  // The two best against each other, in alternating order, twice as many rounds.
+  if (n >= 2) {
+    std::vector<float> ta, tb;
+    for (int r = 0; r < 2 * rounds; ++r) {
+      const Candidate &x = r % 2 ? cand[1] : cand[0], &y = r % 2 ? cand[0] : cand[1];
+      if ((st = hip_status(hipEventRecord(ev[0], s), "hipEventRecord")) != FA_OK) return st;
+      for (int k = 0; k < reps; ++k)
+        if ((st = launch(x)) != FA_OK) return st;
+      if ((st = hip_status(hipEventRecord(ev[1], s), "hipEventRecord")) != FA_OK) return st;
+      for (int k = 0; k < reps; ++k)
+        if ((st = launch(y)) != FA_OK) return st;
+      if ((st = hip_status(hipEventRecord(ev[2], s), "hipEventRecord")) != FA_OK) return st;
+      if ((st = hip_status(hipEventSynchronize(ev[2]), "hipEventSynchronize")) != FA_OK) return st;
+      float mx = 0.f, my = 0.f;
+      if ((st = elapsed(ev[0], ev[1], &mx)) != FA_OK || (st = elapsed(ev[1], ev[2], &my)) != FA_OK) return st;
+      (r % 2 ? tb : ta).push_back(mx / reps);
+      (r % 2 ? ta : tb).push_back(my / reps);
+    }
+    cand[0].ms = median_of(ta);
+    cand[1].ms = median_of(tb);
+    if (cand[1].ms < cand[0].ms) std::swap(cand[0], cand[1]);
+  }
+  g_last_ranking.clear();
+  for (const auto &c : cand) g_last_ranking.push_back(Ranked{cfg_of(*c.e), c.ms});
+  *best = cand[0];
+  return FA_OK;
+}
+
 }  // namespace
+
+namespace fa {
+int fwd_check_args(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int seqlen_q,
+                   int seqlen_k, int n_heads, int n_heads_kv, int d_head, float scale, int causal,
+                   const int32_t *cu_seqlens, int dtype) {
+  return check_args(q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, n_heads_kv, d_head, scale, causal,
+                    cu_seqlens, dtype);
+}
+int set_error(int status, const char *msg) { return fail(status, msg); }
+}  // namespace fa
 
 extern "C" {
 
@@ -291,13 +557,10 @@ int fa_fwd_ext(const void *q, const void *k, const void *v, void *o, float *lse,
   if (st != FA_OK) return st;
   if (num_splits < 0 || num_splits > FA_MAX_SPLITS)
     return fail(FA_ERR_INVALID_ARG, "num_splits must be 0 (automatic) or 1 .. FA_MAX_SPLITS");
-  const bool varlen = cu_seqlens != nullptr;
-  if (num_splits == 0) {
-    num_splits = choose_splits(batch, seqlen_q, seqlen_k, n_heads, d_head, dtype, causal != 0, varlen);
-    while (num_splits > 1 &&
-           (!workspace || workspace_bytes_of(batch, seqlen_q, n_heads, d_head, num_splits) > workspace_bytes))
-      --num_splits;
-  }
+  const Shape shape{batch, seqlen_q, seqlen_k, n_heads, n_heads_kv, d_head, dtype, cu_seqlens != nullptr,
+                    causal != 0};
+  const fa_tile_config_t c = choose_config(shape);
+  if (num_splits == 0) num_splits = splits_within(c, shape, workspace, workspace_bytes);
   if (num_splits > 1) {
     if (!workspace) return fail(FA_ERR_INVALID_ARG, "num_splits > 1 needs a workspace");
     if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
@@ -305,7 +568,6 @@ int fa_fwd_ext(const void *q, const void *k, const void *v, void *o, float *lse,
     if (workspace_bytes < workspace_bytes_of(batch, seqlen_q, n_heads, d_head, num_splits))
       return fail(FA_ERR_INVALID_ARG, "workspace smaller than fa_fwd_workspace_bytes() for num_splits");
   }
-  const fa_tile_config_t c = choose_config(seqlen_q, d_head, dtype, varlen, causal != 0);
   const KernelEntry *e = find_entry(dtype, d_head, c);
   if (!e) return fail(FA_ERR_UNSUPPORTED, "no compiled kernel for the chosen tile configuration");
   const Call call = make_call(q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, n_heads_kv, d_head, scale,
@@ -340,7 +602,8 @@ int fa_fwd_choose_splits(int batch, int seqlen_q, int seqlen_k, int n_heads, int
     return fail(-FA_ERR_INVALID_ARG, "batch, n_heads, seqlen_q and seqlen_k must be >= 1");
   if (!valid_d(d_head)) return fail(-FA_ERR_UNSUPPORTED, "d_head must be 32, 64 or 128");
   ok();
-  return choose_splits(batch, seqlen_q, seqlen_k, n_heads, d_head, dtype, causal != 0, varlen != 0);
+  const Shape shape{batch, seqlen_q, seqlen_k, n_heads, n_heads, d_head, dtype, varlen != 0, causal != 0};
+  return splits_for(choose_config(shape), shape);
 }
 
 size_t fa_bwd_workspace_bytes(int batch, int seqlen_q, int n_heads, int d_head, int atomic_dq) {
@@ -430,7 +693,7 @@ int fa_fwd_get_config(int batch, int seqlen_q, int seqlen_k, int n_heads, int d_
   if (batch < 1 || n_heads < 1 || seqlen_q < 1 || seqlen_k < 1)
     return fail(FA_ERR_INVALID_ARG, "batch, n_heads, seqlen_q and seqlen_k must be >= 1");
   if (!valid_d(d_head)) return fail(FA_ERR_UNSUPPORTED, "d_head must be 32, 64 or 128");
-  *out = choose_config(seqlen_q, d_head, dtype, varlen != 0, false);
+  *out = choose_config(Shape{batch, seqlen_q, seqlen_k, n_heads, n_heads, d_head, dtype, varlen != 0, false});
   return ok();
 }
 
@@ -439,7 +702,26 @@ int fa_fwd_get_config_ext(int batch, int seqlen_q, int seqlen_k, int n_heads, in
   if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
   const int st = fa_fwd_get_config(batch, seqlen_q, seqlen_k, n_heads, d_head, dtype, varlen, out);
   if (st != FA_OK) return st;
-  *out = choose_config(seqlen_q, d_head, dtype, varlen != 0, causal != 0);
+  *out = choose_config(Shape{batch, seqlen_q, seqlen_k, n_heads, n_heads, d_head, dtype, varlen != 0, causal != 0});
+  return ok();
+}
+
+int fa_fwd_query_config(int batch, int seqlen_q, int seqlen_k, int n_heads, int n_heads_kv, int d_head, int dtype,
+                        int varlen, int causal, fa_tile_config_t *out, int *num_splits, int *source) {
+  if (!out) return fail(FA_ERR_INVALID_ARG, "out must be non-null");
+  if (!valid_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "dtype must be FA_BF16 (0) or FA_FP16 (1)");
+  if (batch < 1 || n_heads < 1 || seqlen_q < 1 || seqlen_k < 1)
+    return fail(FA_ERR_INVALID_ARG, "batch, n_heads, seqlen_q and seqlen_k must be >= 1");
+  if (n_heads_kv < 1 || n_heads % n_heads_kv != 0)
+    return fail(FA_ERR_INVALID_ARG, "n_heads_kv must be >= 1 and divide n_heads");
+  if ((varlen != 0 && varlen != 1) || (causal != 0 && causal != 1))
+    return fail(FA_ERR_INVALID_ARG, "varlen and causal must be 0 or 1");
+  if (!valid_d(d_head)) return fail(FA_ERR_UNSUPPORTED, "d_head must be 32, 64 or 128");
+  const Shape shape{batch, seqlen_q, seqlen_k, n_heads, n_heads_kv, d_head, dtype, varlen != 0, causal != 0};
+  int src = kSrcDefault;
+  *out = choose_config(shape, &src);
+  if (num_splits) *num_splits = splits_for(*out, shape);
+  if (source) *source = src;
   return ok();
 }
 
@@ -490,71 +772,91 @@ int fa_fwd_config_resources(int d_head, int dtype, const fa_tile_config_t *cfg, 
   return ok();
 }
 
+int fa_fwd_autotune_ext(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int seqlen_q,
+                        int seqlen_k, int n_heads, int n_heads_kv, int d_head, float scale, int causal,
+                        const int32_t *cu_seqlens, int dtype, int num_splits, void *workspace,
+                        size_t workspace_bytes, void *stream, int rounds, fa_tile_config_t *chosen,
+                        float *best_ms) {
+  int st = check_args(q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, n_heads_kv, d_head, scale, causal,
+                      cu_seqlens, dtype);
+  if (st != FA_OK) return st;
+  if (rounds < 1 || rounds > kMaxTuneRounds) return fail(FA_ERR_INVALID_ARG, "rounds must be 1 .. 100");
+  if (num_splits < 0 || num_splits > FA_MAX_SPLITS)
+    return fail(FA_ERR_INVALID_ARG, "num_splits must be 0 (automatic) or 1 .. FA_MAX_SPLITS");
+  if (workspace && reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(FA_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  if (num_splits > 1 && (!workspace || workspace_bytes < workspace_bytes_of(batch, seqlen_q, n_heads, d_head,
+                                                                             num_splits)))
+    return fail(FA_ERR_INVALID_ARG, "num_splits > 1 needs a workspace of fa_fwd_workspace_bytes() bytes");
+  const Shape shape{batch, seqlen_q, seqlen_k, n_heads, n_heads_kv, d_head, dtype, cu_seqlens != nullptr,
+                    causal != 0};
+  const Call call = make_call(q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, n_heads_kv, d_head, scale,
+                              causal, cu_seqlens, dtype, stream);
+  std::lock_guard<std::mutex> tlk(g_tune_mu);
+  Candidate best;
+  st = tune(call, shape, num_splits, workspace, workspace_bytes, rounds, &best);
+  if (st != FA_OK) return st;
+  bool saved = true;
+  {
+    std::lock_guard<std::mutex> lk(g_cfg_mu);
+    g_tuned[key_of(shape)] = Tuned{cfg_of(*best.e), best.ms};
+    if (const char *path = cache_path()) saved = save_cache_locked(path) == 0;
+  }
+  // Leave O and LSE holding the winner's result.
+  st = launch_entry(*best.e, call, best.splits, workspace);
+  if (st != FA_OK) return st;
+  hipError_t err = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(err));
+  if (chosen) *chosen = cfg_of(*best.e);
+  if (best_ms) *best_ms = best.ms;
+  if (!saved)
+    return fail(FA_ERR_INVALID_ARG, std::string("tuned, but the cache file FA_FWD_TUNE_CACHE=") + cache_path() +
+                                        " could not be written");
+  return ok();
+}
+
 int fa_fwd_autotune(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
                     int seqlen_q, int seqlen_k, int n_heads, int d_head, float scale,
                     const int32_t *cu_seqlens, int dtype, void *stream, int reps,
                     fa_tile_config_t *chosen, float *best_ms) {
-  int st = check_args(q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, n_heads, d_head, scale, 0, cu_seqlens,
-                      dtype);
-  if (st != FA_OK) return st;
-  if (reps < 1) return fail(FA_ERR_INVALID_ARG, "reps must be >= 1");
-  const Call call = make_call(q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, n_heads, d_head, scale, 0,
-                              cu_seqlens, dtype, stream);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipEvent_t e0 = nullptr, e1 = nullptr;
-  auto cleanup = [&] {
-    if (e0) (void)hipEventDestroy(e0);
-    if (e1) (void)hipEventDestroy(e1);
-  };
-  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
-    cleanup();
-    return fail(FA_ERR_HIP, "hipEventCreate failed");
+  return fa_fwd_autotune_ext(q, k, v, o, lse, batch, seqlen_q, seqlen_k, n_heads, n_heads, d_head, scale, 0,
+                             cu_seqlens, dtype, 1, nullptr, 0, stream, reps, chosen, best_ms);
+}
+
+int fa_fwd_tune_ranking(fa_tile_config_t *cfgs, float *ms, int capacity) {
+  if (capacity < 0 || (capacity > 0 && (!cfgs || !ms))) return fail(-FA_ERR_INVALID_ARG, "bad output buffers");
+  std::lock_guard<std::mutex> tlk(g_tune_mu);
+  const int n = (int)g_last_ranking.size();
+  for (int i = 0; i < n && i < capacity; ++i) {
+    cfgs[i] = g_last_ranking[i].cfg;
+    ms[i] = g_last_ranking[i].ms;
   }
-  const KernelEntry *best = nullptr;
-  float best_t = 0.f;
-  for (const auto &e : entries()) {
-    if (e.dtype != dtype || e.d_head != d_head) continue;
-    const fa_tile_config_t c = cfg_of(e);
-    if (lds_bytes_of(d_head, c) > kLdsLimit) continue;  // does not fit one CU's LDS
-    hipFuncAttributes attr;
-    if (hipFuncGetAttributes(&attr, e.kernel) != hipSuccess) continue;
-    if (attr.localSizeBytes > 0) continue;  // spills registers
-    int rc = launch_entry(e, call);
-    if (rc != FA_OK) {
-      cleanup();
-      return rc;
-    }
-    if (hipEventRecord(e0, s) != hipSuccess) break;
-    for (int r = 0; r < reps; ++r)
-      (void)launch_entry(e, call);
-    if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) {
-      cleanup();
-      return fail(FA_ERR_HIP, "event timing failed");
-    }
-    float ms = 0.f;
-    if (hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
-      cleanup();
-      return fail(FA_ERR_HIP, "hipEventElapsedTime failed");
-    }
-    ms /= reps;
-    if (!best || ms < best_t) {
-      best = &e;
-      best_t = ms;
-    }
-  }
-  cleanup();
-  if (!best) return fail(FA_ERR_UNSUPPORTED, "no configuration passed the LDS / spill filter");
-  {
-    std::lock_guard<std::mutex> lk(g_cfg_mu);
-    g_tuned[{d_head, dtype, cu_seqlens ? 1 : 0, 0, log2_bucket(seqlen_q)}] = cfg_of(*best);
-  }
-  // Leave O and LSE holding the winner's result.
-  int rc = launch_entry(*best, call);
-  if (rc != FA_OK) return rc;
-  if (hipStreamSynchronize(s) != hipSuccess) return fail(FA_ERR_HIP, "hipStreamSynchronize failed");
-  if (chosen) *chosen = cfg_of(*best);
-  if (best_ms) *best_ms = best_t;
+  ok();
+  return n;
+}
+
+int fa_fwd_tune_reset(void) {
+  std::lock_guard<std::mutex> tlk(g_tune_mu);
+  std::lock_guard<std::mutex> lk(g_cfg_mu);
+  g_tuned.clear();
+  g_last_ranking.clear();
   return ok();
+}
+
+int fa_fwd_tune_save(const char *path) {
+  if (!path || !*path) return fail(FA_ERR_INVALID_ARG, "path must be a non-empty string");
+  std::lock_guard<std::mutex> lk(g_cfg_mu);
+  if (save_cache_locked(path) != 0) return fail(FA_ERR_INVALID_ARG, std::string("cannot write ") + path);
+  return ok();
+}
+
+int fa_fwd_tune_load(const char *path) {
+  if (!path || !*path) return fail(-FA_ERR_INVALID_ARG, "path must be a non-empty string");
+  std::lock_guard<std::mutex> lk(g_cfg_mu);
+  const int n = load_cache_locked(path);
+  if (n < 0) return fail(-FA_ERR_INVALID_ARG, std::string("cannot read ") + path);
+  ok();
+  return n;
 }
 
 const char *fa_last_error(void) { return g_last_error.c_str(); }

@@ -56,12 +56,21 @@ struct KernelEntry {
   const void *kernel;  // for hipFuncGetAttributes
 };
 
-// Each instantiation unit appends its entries.
-void register_bf16_d32(void (*add)(const KernelEntry &));
-void register_bf16_d64(void (*add)(const KernelEntry &));
-void register_bf16_d128(void (*add)(const KernelEntry &));
-void register_fp16_d32(void (*add)(const KernelEntry &));
-void register_fp16_d64(void (*add)(const KernelEntry &));
-void register_fp16_d128(void (*add)(const KernelEntry &));
+typedef void (*AddEntryFn)(const KernelEntry &);
+
+// Host-side helpers of the C ABI (fa_fwd_api.cpp) for entry points defined in other units.
+// fwd_check_args: fa_fwd_ext's synchronous argument checks (no HIP call); FA_OK or an
+// fa_status_t with the thread's last-error message set.  set_error: set that message and
+// return status.
+int fwd_check_args(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int seqlen_q,
+                   int seqlen_k, int n_heads, int n_heads_kv, int d_head, float scale, int causal,
+                   const int32_t *cu_seqlens, int dtype);
+int set_error(int status, const char *msg);
+
+// The compiled configuration space is split into this many parts per (d_head, dtype); part
+// PART of (D, F16) is compiled in its own unit (fa_fwd_inst.hip) and appends its entries.
+constexpr int kSpaceParts = 4;
+template <int D, bool F16, int PART>
+void register_part(AddEntryFn add);
 
 }  // namespace fa

@@ -17,7 +17,9 @@ FA_MAX_SPLITS = 128
 # Every exported symbol of include/fa_fwd.h.
 EXPORTS = ("fa_fwd", "fa_fwd_ext", "fa_fwd_workspace_bytes", "fa_fwd_choose_splits", "fa_bwd",
            "fa_bwd_workspace_bytes",
-           "fa_fwd_autotune", "fa_fwd_set_config", "fa_fwd_get_config", "fa_fwd_get_config_ext", "fa_fwd_num_configs", "fa_fwd_list_configs", "fa_fwd_config_lds_bytes",
+           "fa_fwd_autotune", "fa_fwd_autotune_ext", "fa_fwd_tune_ranking", "fa_fwd_tune_reset", "fa_fwd_tune_save",
+           "fa_fwd_tune_load", "fa_fwd_set_config", "fa_fwd_get_config", "fa_fwd_get_config_ext",
+           "fa_fwd_query_config", "fa_fwd_num_configs", "fa_fwd_list_configs", "fa_fwd_config_lds_bytes",
            "fa_fwd_config_resources", "fa_last_error", "fa_version")
 
 
@@ -72,6 +74,21 @@ def lib():
         L.fa_fwd_autotune.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.c_float, _vp,
                                       _i, _vp, _i, ctypes.POINTER(TileConfig),
                                       ctypes.POINTER(ctypes.c_float)]
+        L.fa_fwd_autotune_ext.restype = _i
+        L.fa_fwd_autotune_ext.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, ctypes.c_float, _i, _vp,
+                                          _i, _i, _vp, ctypes.c_size_t, _vp, _i, ctypes.POINTER(TileConfig),
+                                          ctypes.POINTER(ctypes.c_float)]
+        L.fa_fwd_tune_ranking.restype = _i
+        L.fa_fwd_tune_ranking.argtypes = [ctypes.POINTER(TileConfig), ctypes.POINTER(ctypes.c_float), _i]
+        L.fa_fwd_tune_reset.restype = _i
+        L.fa_fwd_tune_reset.argtypes = []
+        L.fa_fwd_tune_save.restype = _i
+        L.fa_fwd_tune_save.argtypes = [ctypes.c_char_p]
+        L.fa_fwd_tune_load.restype = _i
+        L.fa_fwd_tune_load.argtypes = [ctypes.c_char_p]
+        L.fa_fwd_query_config.restype = _i
+        L.fa_fwd_query_config.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i, _i, ctypes.POINTER(TileConfig),
+                                          ctypes.POINTER(_i), ctypes.POINTER(_i)]
         L.fa_fwd_set_config.restype = _i
         L.fa_fwd_set_config.argtypes = [_i, _i, ctypes.POINTER(TileConfig)]
         L.fa_fwd_get_config.restype = _i
@@ -294,19 +311,72 @@ def fa_fwd_choose_splits(batch, seqlen_q, seqlen_k, n_heads, d_head, dtype, caus
 
 
 def fa_fwd_autotune(q, k, v, o, lse, scale=None, cu_seqlens=None, max_seqlen=None, reps=5, stream=None):
-    """Time every admissible compiled configuration on these buffers; returns (TileConfig, ms)."""
-    batch, nq, nk, heads, _, d = _shape_args(q, k, v, cu_seqlens, max_seqlen)
+    """Tune an fa_fwd call (reps = interleaved rounds) on these buffers; returns (TileConfig, ms)."""
+    return fa_fwd_autotune_ext(q, k, v, o, lse, scale=scale, cu_seqlens=cu_seqlens, max_seqlen=max_seqlen,
+                               rounds=reps, stream=stream)
+
+
+def fa_fwd_autotune_ext(q, k, v, o, lse, scale=None, causal=False, cu_seqlens=None, max_seqlen=None,
+                        num_splits=1, workspace=None, rounds=5, stream=None):
+    """Tune an fa_fwd_ext call of this kind on these buffers (interleaved median timing of every
+    compiled configuration); returns (TileConfig, median ms per launch of the winner)."""
+    batch, nq, nk, heads, heads_kv, d = _shape_args(q, k, v, cu_seqlens, max_seqlen, grouped=True)
+    _check_tensors(q, k, v, cu_seqlens)
     if scale is None:
         scale = d ** -0.5
+    o, lse = _outputs(q, o, lse, batch, heads, nq)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if not workspace.is_cuda:
+            raise ValueError("workspace must be a device tensor")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     chosen = TileConfig()
     ms = ctypes.c_float()
-    st = lib().fa_fwd_autotune(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                               batch, nq, nk, heads, d, float(scale),
-                               cu_seqlens.data_ptr() if cu_seqlens is not None else None,
-                               _dtype_code(q), _stream_handle(stream, q.device), int(reps),
-                               ctypes.byref(chosen), ctypes.byref(ms))
+    st = lib().fa_fwd_autotune_ext(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                   batch, nq, nk, heads, heads_kv, d, float(scale), int(bool(causal)),
+                                   cu_seqlens.data_ptr() if cu_seqlens is not None else None, _dtype_code(q),
+                                   int(num_splits), ws_ptr, ws_bytes, _stream_handle(stream, q.device),
+                                   int(rounds), ctypes.byref(chosen), ctypes.byref(ms))
     _check(st)
     return chosen, ms.value
+
+
+def fa_fwd_tune_ranking():
+    """The last tuning's candidates, fastest first: [(TileConfig, median ms), ...]."""
+    n = lib().fa_fwd_tune_ranking(None, None, 0)
+    if n < 0:
+        raise FaError(-n, fa_last_error())
+    cfgs, ms = (TileConfig * max(n, 1))(), (ctypes.c_float * max(n, 1))()
+    lib().fa_fwd_tune_ranking(cfgs, ms, n)
+    return [(cfgs[i], ms[i]) for i in range(n)]
+
+
+def fa_fwd_tune_reset():
+    return _check(lib().fa_fwd_tune_reset())
+
+
+def fa_fwd_tune_save(path):
+    return _check(lib().fa_fwd_tune_save(os.fsencode(path)))
+
+
+def fa_fwd_tune_load(path):
+    n = lib().fa_fwd_tune_load(os.fsencode(path))
+    if n < 0:
+        raise FaError(-n, fa_last_error())
+    return n
+
+
+CONFIG_SOURCES = {0: "default", 1: "tuned", 2: "FA_FWD_CONFIG", 3: "forced"}
+
+
+def fa_fwd_query_config(batch, seqlen_q, seqlen_k, n_heads, d_head, dtype, n_heads_kv=None, varlen=False,
+                        causal=False):
+    """(TileConfig, automatic split count, source) fa_fwd_ext would use for this call kind."""
+    c, n, src = TileConfig(), _i(), _i()
+    _check(lib().fa_fwd_query_config(batch, seqlen_q, seqlen_k, n_heads, n_heads if n_heads_kv is None else n_heads_kv,
+                                     d_head, dtype, int(bool(varlen)), int(bool(causal)), ctypes.byref(c),
+                                     ctypes.byref(n), ctypes.byref(src)))
+    return c, n.value, CONFIG_SOURCES[src.value]
 
 
 def fa_fwd_set_config(d_head, dtype, cfg):

@@ -189,27 +189,73 @@ size_t fa_bwd_workspace_bytes(int batch, int seqlen_q, int n_heads, int d_head, 
 
 /* Tile autotuner (page "Flash Attention 2 Chapter6", Kernel 7: enumerate the
  * configuration space, drop configurations that spill registers or do not
- * fit, time the rest, keep the best).  Runs every compiled configuration for
- * (dtype, d_head) that fits the LDS budget and does not spill, `reps` timed
- * launches each after one warm-up, on the caller's buffers and stream (O and
- * LSE are overwritten; the last launch uses the chosen configuration, so
- * they hold its result).  Synchronises `stream`.  The winner is remembered
- * for this (dtype, d_head, varlen, seqlen_q bucket) and used by later fa_fwd
- * calls of that shape class (unless fa_fwd_set_config overrides it).
- * chosen (may be NULL) receives the winner, best_ms (may be NULL) its
- * average time per launch in milliseconds.  Arguments are checked as in
- * fa_fwd; reps must be >= 1. */
+ * fit, time the rest, keep the best).  The space is every compiled
+ * configuration of (dtype, d_head): B_r in {64, 128, 256} x B_c in
+ * {32, 64, 128} x wavefronts x K/V stages x schedule, less those over the
+ * 160 KB LDS budget or that spill (fa_fwd_num_configs / fa_fwd_list_configs
+ * list it).  Arguments and checks are fa_fwd_ext's; the call's kind --
+ * n_heads_kv, causal, packed or dense, num_splits (0 = each candidate's
+ * automatic count, lowered to what workspace holds) -- is tuned as given, on
+ * the caller's buffers and stream.
+ *
+ * Timing: the default configuration is launched for about 40 ms first, so
+ * the clock reaches its loaded state; then `rounds` (1 .. 100) interleaved
+ * rounds each time every candidate once (enough launches per sample for
+ * about 0.5 ms), the order rotating by one per round; a candidate's score is
+ * its median time per launch.  The two best are then timed against each
+ * other for 2 x rounds more rounds, alternating which goes first, and the
+ * faster median wins.
+ *
+ * The winner is remembered for calls of the same kind and size class:
+ * (d_head, dtype, packed, causal, ceil(log2(n_heads / n_heads_kv)),
+ * ceil(log2 seqlen_q), ceil(log2(batch x n_heads))), and fa_fwd / fa_fwd_ext
+ * use it unless a forced configuration applies (fa_fwd_set_config,
+ * FA_FWD_CONFIG).  When the environment variable FA_FWD_TUNE_CACHE names a
+ * file, the remembered choices are read from it at the first configuration
+ * lookup and the file is rewritten after every tuning (FA_ERR_INVALID_ARG,
+ * with the choice still remembered, if it cannot be written).
+ * O and LSE are overwritten; the last launch uses the winner, so they hold
+ * its result.  Synchronises `stream`.  chosen and best_ms (either may be
+ * NULL) receive the winner and its median time per launch in ms.  A failed
+ * HIP call (launch, event) returns FA_ERR_HIP. */
+int fa_fwd_autotune_ext(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
+                        int seqlen_q, int seqlen_k, int n_heads, int n_heads_kv, int d_head, float scale,
+                        int causal, const int32_t *cu_seqlens, int dtype, int num_splits, void *workspace,
+                        size_t workspace_bytes, void *stream, int rounds, fa_tile_config_t *chosen,
+                        float *best_ms);
+
+/* fa_fwd_autotune_ext for an fa_fwd call: n_heads_kv = n_heads, causal 0,
+ * no split; `reps` is the number of rounds. */
 int fa_fwd_autotune(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
                     int seqlen_q, int seqlen_k, int n_heads, int d_head, float scale,
                     const int32_t *cu_seqlens, int dtype, void *stream, int reps,
                     fa_tile_config_t *chosen, float *best_ms);
 
+/* The last tuning's candidates, fastest first (the two best with their
+ * head-to-head medians): copies up to `capacity` configurations and median
+ * ms per launch; returns how many there were (0 before any tuning; < 0 on
+ * bad arguments).  Host-only. */
+int fa_fwd_tune_ranking(fa_tile_config_t *cfgs, float *ms, int capacity);
+
+/* Forget every remembered tuning result (the cache file is left alone).  Host-only. */
+int fa_fwd_tune_reset(void);
+
+/* Write the remembered tuning results to `path` in the FA_FWD_TUNE_CACHE
+ * format (one line per choice).  FA_ERR_INVALID_ARG if it cannot be written.
+ * Host-only. */
+int fa_fwd_tune_save(const char *path);
+
+/* Merge tuning results from a file in that format; lines for configurations
+ * this build lacks are skipped.  Returns the number of choices taken, or
+ * -FA_ERR_INVALID_ARG if the file cannot be read.  Host-only. */
+int fa_fwd_tune_load(const char *path);
+
 /* Force the configuration fa_fwd uses for (d_head, dtype); cfg == NULL
  * returns to automatic choice.  Automatic choice, in order: the environment
  * variable FA_FWD_CONFIG="br,bc,waves,stages,schedule" (read once; applies
  * to every (d_head, dtype) that has that configuration compiled), then a
- * configuration fa_fwd_autotune chose for this shape class, then the
- * built-in default.  FA_ERR_UNSUPPORTED if no kernel was compiled for cfg. */
+ * configuration the autotuner chose for this call's kind and size class,
+ * then the built-in default.  FA_ERR_UNSUPPORTED if no kernel was compiled for cfg. */
 int fa_fwd_set_config(int d_head, int dtype, const fa_tile_config_t *cfg);
 
 /* The configuration fa_fwd would use for this shape (host-only lookup).
@@ -221,6 +267,16 @@ int fa_fwd_get_config(int batch, int seqlen_q, int seqlen_k, int n_heads, int d_
  * configuration fa_fwd_ext would use (host-only lookup). */
 int fa_fwd_get_config_ext(int batch, int seqlen_q, int seqlen_k, int n_heads, int d_head, int dtype,
                           int varlen, int causal, fa_tile_config_t *out);
+
+/* The configuration and automatic split count fa_fwd_ext would use for a call
+ * of this shape and kind (varlen, causal 0 or 1; n_heads_kv divides n_heads),
+ * and where the configuration comes from: *source = 0 the built-in default,
+ * 1 a tuned choice, 2 FA_FWD_CONFIG, 3 fa_fwd_set_config.  num_splits and
+ * source may be NULL; the split count is before lowering to a workspace.
+ * Host-only lookup. */
+int fa_fwd_query_config(int batch, int seqlen_q, int seqlen_k, int n_heads, int n_heads_kv, int d_head,
+                        int dtype, int varlen, int causal, fa_tile_config_t *out, int *num_splits,
+                        int *source);
 
 /* Number of compiled configurations for (d_head, dtype); < 0 on bad args. */
 int fa_fwd_num_configs(int d_head, int dtype);

@@ -42,6 +42,13 @@ def _gpu():
     torch.cuda.synchronize()
 
 
+@pytest.fixture(autouse=True)
+def _forget_tuning():
+    # the benchmark's launch path tunes; no tuned choice outlives its test
+    yield
+    fa.fa_fwd_tune_reset()
+
+
 def _launch_as_benchmarked(name):
     """Run the workload once the way bench.py times it, with O and LSE pre-filled with NaN.
     Returns (workload, O on the host, LSE on the host, the launch description)."""

@@ -278,8 +278,11 @@ def test_autotune_picks_a_compiled_config_and_leaves_valid_output():
     assert ms > 0
     o_r, lse_r = oracle.attention(inputs.to_f64(q), inputs.to_f64(k), inputs.to_f64(v), 128 ** -0.5)
     assert_close(o.cpu().double().numpy(), o_r, lse.cpu().double().numpy(), lse_r, "autotuned")
-    got = fa.fa_fwd_get_config(2, 512, 512, 4, 128, fa.FA_BF16)
-    assert got.as_tuple() == chosen.as_tuple()
+    try:
+        got = fa.fa_fwd_get_config(2, 512, 512, 4, 128, fa.FA_BF16)
+        assert got.as_tuple() == chosen.as_tuple()
+    finally:
+        fa.fa_fwd_tune_reset()
 
 
 @pytest.mark.parametrize("d", [32, 64, 128])
