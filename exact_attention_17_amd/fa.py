@@ -15,7 +15,7 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_MISALIGNED, FA_ERR_HIP = 0
 FA_MAX_SPLITS = 128
 
 # Every exported symbol of include/fa_fwd.h.
-EXPORTS = ("fa_fwd", "fa_fwd_ext", "fa_fwd_workspace_bytes", "fa_fwd_choose_splits", "fa_bwd",
+EXPORTS = ("fa_fwd", "fa_fwd_ext", "fa_fwd_ext_noalloc", "fa_fwd_workspace_bytes", "fa_fwd_choose_splits", "fa_bwd",
            "fa_bwd_workspace_bytes",
            "fa_fwd_autotune", "fa_fwd_autotune_ext", "fa_fwd_tune_ranking", "fa_fwd_tune_reset", "fa_fwd_tune_save",
            "fa_fwd_tune_load", "fa_fwd_set_config", "fa_fwd_get_config", "fa_fwd_get_config_ext",
@@ -61,6 +61,9 @@ def lib():
         L.fa_fwd_ext.restype = _i
         L.fa_fwd_ext.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, ctypes.c_float, _i, _vp, _i,
                                  _i, _vp, ctypes.c_size_t, _vp]
+        L.fa_fwd_ext_noalloc.restype = _i
+        L.fa_fwd_ext_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, ctypes.c_float, _i, _vp,
+                                         _i, _i, _vp]
         L.fa_fwd_workspace_bytes.restype = ctypes.c_size_t
         L.fa_fwd_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
         L.fa_fwd_choose_splits.restype = _i
@@ -246,6 +249,29 @@ def fa_fwd_ext(q, k, v, o=None, lse=None, scale=None, causal=False, cu_seqlens=N
                           nk, heads, heads_kv, d, float(scale), int(bool(causal)),
                           cu_seqlens.data_ptr() if cu_seqlens is not None else None, _dtype_code(q),
                           int(num_splits), ws_ptr, ws_bytes, _stream_handle(stream, q.device))
+    _check(st)
+    return o, lse
+
+
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def fa_fwd_ext_noalloc(q, k, v, o, lse, scale=None, causal=False, cu_seqlens=None, max_seqlen=None,
+                       num_splits=0, stream=None):
+    """fa_fwd_ext without a workspace: split scratch comes from the library's static device
+    array (FA_NOALLOC_SCRATCH_BYTES per GPU).  o and lse must be given (nothing is
+    allocated).  Returns (o, lse)."""
+    if o is None or lse is None:
+        raise ValueError("fa_fwd_ext_noalloc writes into caller-supplied o and lse")
+    batch, nq, nk, heads, heads_kv, d = _shape_args(q, k, v, cu_seqlens, max_seqlen, grouped=True)
+    _check_tensors(q, k, v, cu_seqlens)
+    if scale is None:
+        scale = d ** -0.5
+    o, lse = _outputs(q, o, lse, batch, heads, nq)
+    st = lib().fa_fwd_ext_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), batch,
+                                  nq, nk, heads, heads_kv, d, float(scale), int(bool(causal)),
+                                  cu_seqlens.data_ptr() if cu_seqlens is not None else None, _dtype_code(q),
+                                  int(num_splits), _stream_handle(stream, q.device))
     _check(st)
     return o, lse
 

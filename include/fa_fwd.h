@@ -151,6 +151,27 @@ size_t fa_fwd_workspace_bytes(int batch, int seqlen_q, int n_heads, int d_head, 
 int fa_fwd_choose_splits(int batch, int seqlen_q, int seqlen_k, int n_heads, int d_head, int dtype,
                          int causal, int varlen);
 
+/* Bytes of the device array fa_fwd_ext_noalloc takes its split scratch from (16 MiB). */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* fa_fwd_ext for callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Arguments, layouts, results and
+ * errors as fa_fwd_ext, without the workspace: a split call's scratch (the per-split fp32
+ * partial outputs and LSE rows) is a library-owned device array of FA_NOALLOC_SCRATCH_BYTES
+ * per GPU, held from library load until the process ends.  The call allocates nothing and
+ * calls no allocating routine.
+ *  - num_splits > 1 needing more than FA_NOALLOC_SCRATCH_BYTES
+ *    (fa_fwd_workspace_bytes(...) > it) -> FA_ERR_INVALID_ARG with a message naming both
+ *    sizes; num_splits = 0 lowers the automatic count to what the array holds.
+ *  - All calls on one GPU share its array and it keeps the last call's contents (nothing in
+ *    it has to start at zero).  Calls that overlap in time on one GPU race on it: issue them
+ *    on one stream, or serialise them.
+ *  - The first call on a device resolves the array's device address (hipGetSymbolAddress,
+ *    with that device current); a failure there -> FA_ERR_HIP. */
+int fa_fwd_ext_noalloc(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
+                       int seqlen_q, int seqlen_k, int n_heads, int n_heads_kv, int d_head, float scale,
+                       int causal, const int32_t *cu_seqlens, int dtype, int num_splits, void *stream);
+
 /* Backward pass (page "GPU 内核与 FlashAttention", section 13; FlashAttention-2's
  * parallelisation over K/V tiles, section 14.2).  Given the forward's inputs,
  * its output o and natural-log lse (from fa_fwd or fa_fwd_ext with the same

@@ -249,6 +249,45 @@ def test_bwd_workspace_bytes_and_bad_arguments():
         assert fa.fa_last_error() != ""
 
 
+def call_noalloc(**over):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, batch=8, seqlen_q=512, seqlen_k=512, n_heads=16, n_heads_kv=16,
+                d_head=128, scale=0.125, causal=0, cu_seqlens=None, dtype=fa.FA_BF16, num_splits=4, stream=None)
+    args.update(over)
+    return fa.lib().fa_fwd_ext_noalloc(args["q"], args["k"], args["v"], args["o"], args["lse"], args["batch"],
+                                       args["seqlen_q"], args["seqlen_k"], args["n_heads"], args["n_heads_kv"],
+                                       args["d_head"], ctypes.c_float(args["scale"]), args["causal"],
+                                       args["cu_seqlens"], args["dtype"], args["num_splits"], args["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(n_heads_kv=3), fa.FA_ERR_INVALID_ARG),
+    (dict(num_splits=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(num_splits=fa.FA_MAX_SPLITS + 1), fa.FA_ERR_INVALID_ARG),
+    (dict(d_head=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(o=A + 8), fa.FA_ERR_MISALIGNED),
+])
+def test_noalloc_bad_arguments_rejected_on_host(over, status):
+    assert call_noalloc(**over) == status
+    assert fa.fa_last_error() != ""
+
+
+def test_noalloc_rejects_splits_beyond_its_static_scratch_on_host():
+    # 8 x 16 heads x 512 rows x 129 floats x 4 bytes = 33.8 MB per split: even 1 split's
+    # worth exceeds 16 MiB, so any count > 1 is refused before the device is touched
+    need = fa.fa_fwd_workspace_bytes(8, 512, 16, 128, 4)
+    assert need > fa.FA_NOALLOC_SCRATCH_BYTES
+    assert call_noalloc(num_splits=4) == fa.FA_ERR_INVALID_ARG
+    msg = fa.fa_last_error()
+    assert str(need) in msg and str(fa.FA_NOALLOC_SCRATCH_BYTES) in msg
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    assert re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \(16u << 20\)", text)
+    assert fa.FA_NOALLOC_SCRATCH_BYTES == 16 << 20
+
+
 def test_tune_cache_save_load_reset_host_only(tmp_path):
     fa.fa_fwd_tune_reset()
     try:
