@@ -376,8 +376,14 @@ __device__ __forceinline__ void pvqk_block(const char *sv, const i32x4 (&P)[BC /
 template <int KB>
 struct RowSum {
   static constexpr int NP = KB >= 2 ? 4 : 1;
-  float v[NP] = {};
-  __device__ __forceinline__ void add(int i, float x) { v[i % NP] += x; }
+  float v[NP];
+  // the first NP terms start the sums (0 + x is x exactly for these terms, all >= 0)
+  __device__ __forceinline__ void add(int i, float x) {
+    if (i < NP)
+      v[i] = x;
+    else
+      v[i % NP] += x;
+  }
   __device__ __forceinline__ float total() const {
     if constexpr (NP == 4) return (v[0] + v[1]) + (v[2] + v[3]);
     return v[0];
@@ -668,8 +674,6 @@ fa_fwd_kernel(FaArgs a) {
   const char *vb = (const char *)a.v + (krow0 * hkd + (int64_t)hk * D) * 2;
   char *ob = (char *)a.o + (qrow0 * hd + (int64_t)h * D) * 2;
   const auto rq = make_rsrc(qb, (uint32_t)(nq - 1) * row_bytes + ROWB);
-  const auto rk = make_rsrc(kb_, (uint32_t)(nk - 1) * kv_row_bytes + ROWB);
-  const auto rv = make_rsrc(vb, (uint32_t)(nk - 1) * kv_row_bytes + ROWB);
   const auto ro = make_rsrc(ob, (uint32_t)(nq - 1) * row_bytes + ROWB);
   const int64_t lse_base = ((int64_t)b * a.heads + h) * a.seqlen_q;
   float *lse_row = a.lse + lse_base;
@@ -701,10 +705,15 @@ fa_fwd_kernel(FaArgs a) {
   // by one wavefront instruction; lane i's 16 bytes land at piece + 16 i, so each lane
   // fetches the global chunk that the swizzled layout puts there.  LW wavefronts share the
   // pieces, this one being number lw among them.
-  auto load_by = [&](const __amdgpu_buffer_rsrc_t &rsrc, char *dst, int j, int lw, auto lw_c)
-                     __attribute__((always_inline)) {
+  // The tile's offset goes into the buffer resource (base advanced, range shortened: scalar
+  // work) rather than into every lane's offset, so that the per-lane offsets are the same for
+  // every tile and no vector instruction is spent on them.  The range check still bounds the
+  // sequence: tile j starts below its end (it holds a key), and rows past the end read as zero.
+  const uint32_t kv_bytes = (uint32_t)(nk - 1) * kv_row_bytes + ROWB;
+  auto load_by = [&](const char *base, char *dst, int j, int lw, auto lw_c) __attribute__((always_inline)) {
     constexpr int LW = decltype(lw_c)::value;
     const uint32_t tile_off = (uint32_t)(j * BC) * kv_row_bytes;
+    const auto rsrc = make_rsrc(base + tile_off, kv_bytes - tile_off);
 #pragma unroll
     for (int i = 0; i < (NCH + LW - 1) / LW; ++i) {
       const int u = lw + i * LW;
@@ -712,13 +721,13 @@ fa_fwd_kernel(FaArgs a) {
         const int pos = u * 1024 + lane * 16;
         const int r = pos / ROWB;
         const int cc = ((pos % ROWB) >> 4) ^ swz<D>(r);
-        const uint32_t goff = tile_off + (uint32_t)r * kv_row_bytes + cc * 16;
+        const uint32_t goff = (uint32_t)r * kv_row_bytes + cc * 16;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void FA_LDS *)(dst + u * 1024), 16, goff, 0, 0, 0);
       }
     }
   };
-  auto load_one = [&](const __amdgpu_buffer_rsrc_t &rsrc, char *dst, int j) __attribute__((always_inline)) {
-    load_by(rsrc, dst, j, wave, std::integral_constant<int, NW>{});
+  auto load_one = [&](const char *base, char *dst, int j) __attribute__((always_inline)) {
+    load_by(base, dst, j, wave, std::integral_constant<int, NW>{});
   };
 
   f32x16 O[NB][DT];
@@ -774,8 +783,8 @@ fa_fwd_kernel(FaArgs a) {
       if constexpr (STAGES == 1) {
         if (j > 0) {
           __syncthreads();  // everyone is done with tile j-1
-          load_one(rk, smem, jb + j);
-          load_one(rv, smem + TILE, jb + j);
+          load_one(kb_, smem, jb + j);
+          load_one(vb, smem + TILE, jb + j);
         }
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       } else {
@@ -796,8 +805,8 @@ fa_fwd_kernel(FaArgs a) {
       if constexpr (STAGES >= 2) {
         constexpr int NS = (ST + STAGES - 1) % STAGES;  // stage of tile j + STAGES - 1
         if (j + STAGES - 1 < ntl) {
-          load_one(rk, smem + NS * STAGE, jb + j + STAGES - 1);
-          load_one(rv, smem + NS * STAGE + TILE, jb + j + STAGES - 1);
+          load_one(kb_, smem + NS * STAGE, jb + j + STAGES - 1);
+          load_one(vb, smem + NS * STAGE + TILE, jb + j + STAGES - 1);
         }
       }
       // (an unmasked tile has a key visible to every row of the wavefront; a masked one may
@@ -836,8 +845,8 @@ fa_fwd_kernel(FaArgs a) {
 #pragma unroll
     for (int t = 0; t < (STAGES > 1 ? STAGES - 1 : 1); ++t) {
       if (t < ntl) {
-        load_one(rk, smem + t * STAGE, jb + t);
-        load_one(rv, smem + t * STAGE + TILE, jb + t);
+        load_one(kb_, smem + t * STAGE, jb + t);
+        load_one(vb, smem + t * STAGE + TILE, jb + t);
       }
     }
     run(std::false_type{}, 0, jm);
@@ -859,15 +868,15 @@ fa_fwd_kernel(FaArgs a) {
     auto kslot = [&](int j) __attribute__((always_inline)) { return smem + (j & 1) * TILE; };
     auto vslot = [&](int j) __attribute__((always_inline)) { return smem + 2 * TILE + (j % 3) * TILE; };
     if (ntl > 0) {
-      load_one(rk, kslot(0), jb);
-      load_one(rv, vslot(0), jb);
+      load_one(kb_, kslot(0), jb);
+      load_one(vb, vslot(0), jb);
     }
     for (int j = 0; j <= ntl; ++j) {
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
       if (j + 1 < ntl) {
-        load_one(rk, kslot(j + 1), jb + j + 1);
-        load_one(rv, vslot(j + 1), jb + j + 1);
+        load_one(kb_, kslot(j + 1), jb + j + 1);
+        load_one(vb, vslot(j + 1), jb + j + 1);
       }
       // 1.
       if (j < ntl) qk_block<D, BC, F16>(kslot(j), S[0], qreg[0], ad);
@@ -912,8 +921,8 @@ fa_fwd_kernel(FaArgs a) {
     i32x4 P[KS];
     char *const kbase = smem + 3 * TILE;  // K slots; V slots at smem
     for (int t = 0; t < 2; ++t)
-      if (t < ntl) load_one(rk, kbase + t * TILE, jb + t);
-    if (ntl > 0) load_one(rv, smem, jb);
+      if (t < ntl) load_one(kb_, kbase + t * TILE, jb + t);
+    if (ntl > 0) load_one(vb, smem, jb);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     wg_barrier();
     if (grp == 1) wg_barrier();
@@ -938,9 +947,9 @@ fa_fwd_kernel(FaArgs a) {
       if (grp == 1) wait_vmcnt<0>();  // V(j), issued in the previous step, landed
       wg_barrier();
       if (grp == 0) {
-        if (j + 2 < ntl) load_by(rk, kbase + SP * TILE, jb + j + 2, gw, Four{});
+        if (j + 2 < ntl) load_by(kb_, kbase + SP * TILE, jb + j + 2, gw, Four{});
       } else {
-        if (j + 1 < ntl) load_by(rv, smem + SN * TILE, jb + j + 1, gw, Four{});
+        if (j + 1 < ntl) load_by(vb, smem + SN * TILE, jb + j + 1, gw, Four{});
       }
       if constexpr (PH != 2) {
         bool rs;
