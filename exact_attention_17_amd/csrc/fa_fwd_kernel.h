@@ -66,6 +66,17 @@
 //    first: the ping-pong of page "GPU 内核与 FlashAttention", section 15.3,
 //    with one barrier in place of named barriers.  The matrix half's two products
 //    form one MFMA stream, so LDS reads for QK^T overlap the end of PV.
+//  SCHED 5: twelve wavefronts in three groups of four (one of each per SIMD), 32-key
+//    tiles, three wavefronts per SIMD.  Barriers split each step into a matrix phase and two
+//    softmax phases, and the groups run one phase apart: in every phase one group issues
+//    matrix instructions while the other two are in the two parts of their softmax.  A
+//    wavefront issues vector instructions at well under the SIMD's rate (about one per 5
+//    cycles alone on gfx950; two wavefronts side by side each keep that rate), so giving the
+//    softmax two phases and two wavefronts the vector unit keeps it off the critical path.
+//    Measured at d_head 128 (16 x 4096 x 16 heads) it is about a tenth slower than SCHED 2:
+//    it pays three barriers and a phase hand-off per 32 keys where SCHED 2 pays two per 64,
+//    and that costs more than the second vector issuer gains.  The autotuner keeps it in
+//    its space.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -579,7 +590,7 @@ __device__ __forceinline__ void store_block_part(const f32x16 (&O)[D / 32], floa
 
 template <int SCHED>
 constexpr int waves_per_simd() {
-  return SCHED == 1 ? 1 : SCHED == 4 ? 3 : 2;
+  return SCHED == 1 ? 1 : (SCHED == 4 || SCHED == 5) ? 3 : 2;
 }
 
 // Workgroup barrier without the memory fences of __syncthreads (which would also wait for
@@ -610,7 +621,7 @@ fa_fwd_kernel(FaArgs a) {
   static_assert(BC % 32 == 0 && TILE % 1024 == 0, "tile shape");
   static_assert(STAGES >= 1 && STAGES <= 4, "stages");
   static_assert(SCHED == 0 || (SCHED == 1 && STAGES == 2) || (SCHED == 2 && STAGES == 3 && NW == 8) ||
-                    (SCHED == 4 && BC == 32),
+                    (SCHED == 4 && BC == 32) || (SCHED == 5 && STAGES == 3 && NW == 12),
                 "schedule");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
@@ -898,6 +909,117 @@ fa_fwd_kernel(FaArgs a) {
     }
     finish(0);
     finish(1);
+  } else if constexpr (SCHED == 5) {
+    // Three-group rotation (see the header comment): twelve wavefronts, three groups of four
+    // (one wavefront of each group per SIMD).  Every wavefront runs the same program,
+    //   step j = MMA(j) | barrier | SM1(j) | barrier | SM2(j) | barrier,
+    // MMA(j) = PV(j-1) + QK(j), SM1 the speculative exponentials, row sum and check (or the
+    // plain step), SM2 the 16-bit packing and the rescale of O; group g starts g barriers
+    // later.  Between two barriers (a phase) one group issues matrix instructions while the
+    // two others are in the two parts of their softmax, so a softmax has two phases to finish
+    // and two wavefronts per SIMD issue vector instructions side by side.  With group g's
+    // step j in phases 3j+g .. 3j+g+2: K(j) and V(j-1) are read in phases 3j .. 3j+2.  Rings
+    // of three slots (tile t in slot t % 3; V slots first, then K slots).  Group 0 issues
+    // K(j+2) at the start of phase 3j+1 (into the slot of K(j-1), last read in phase 3j-1)
+    // and waits for K(j+1) at the end of phase 3j+2; group 1 issues V(j+1) at the start of
+    // phase 3j+2 (into the slot of V(j-2), last read in phase 3j-1) and waits for V(j) at the
+    // end of the same phase; each wait is at least one barrier ahead of the tile's first read.
+    const int grp = wave >> 2;  // 0, 1, 2
+    const int gw = wave & 3;
+    using Four = std::integral_constant<int, 4>;
+    constexpr int LPT = NCH >= 4 ? NCH / 4 : 1;  // loads per tile of a loading wavefront
+    static_assert(NCH % 4 == 0 || 4 % NCH == 0, "tile pieces spread evenly");
+    f32x16 S[KB];
+    i32x4 P[KS];
+    float alpha = 1.f;
+    bool rs = false;
+    char *const kbase = smem + 3 * TILE;  // K slots; V slots at smem
+    for (int t = 0; t < 2; ++t)
+      if (t < ntl) load_one(kb_, kbase + t * TILE, jb + t);
+    if (ntl > 0) load_one(vb, smem, jb);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    wg_barrier();
+    if (grp >= 1) wg_barrier();
+    if (grp == 2) wg_barrier();
+    // Step j in slot ST = j % 3; phase PH as in schedule 2 (0: QK^T only, 1: PV and QK^T,
+    // 2: PV only), the first and last steps outside the loops.
+    auto step = [&](auto st_c, auto mask_c, auto ph_c, int j) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st_c)::value;
+      constexpr bool MK = decltype(mask_c)::value;
+      constexpr int PH = decltype(ph_c)::value;
+      constexpr int SP = (ST + 2) % 3;  // slot of tile j - 1 (and of tile j + 2)
+      constexpr int SN = (ST + 1) % 3;  // slot of tile j + 1
+      if constexpr (PH == 1) {
+        pvqk_block<D, BC, F16, 3, SP * TILE, ST * TILE>(smem, P, O[0], kbase, S, qreg[0], ad);
+      } else if constexpr (PH == 0) {
+        qk_block<D, BC, F16, 3, ST * TILE>(kbase, S, qreg[0], ad);
+      } else {
+        pv_block<D, BC, F16, 2, SP * TILE>(smem, P, O[0], ad);
+      }
+      wg_barrier();
+      // SM1
+      if (grp == 0) {
+        if (j + 2 < ntl) load_by(kb_, kbase + SP * TILE, jb + j + 2, gw, Four{});
+      } else if (grp == 1) {
+        if (j + 1 < ntl) load_by(vb, smem + SN * TILE, jb + j + 1, gw, Four{});
+      }
+      if constexpr (PH != 2) {
+        alpha = MK ? softmax_block<BC, F16, true>(S, P, m[0], l[0], c, klim[0] - (jb + j) * BC - 4 * hi, rs)
+                   : softmax_block_spec<BC, F16>(S, P, m[0], l[0], c, rs);
+        lds_dep(l[0]);
+      }
+      if (grp == 1) {
+        // V(j) landed (V(j+1), issued above, may still be in flight)
+        if (j + 1 < ntl)
+          wait_vmcnt<LPT>();
+        else
+          wait_vmcnt<0>();
+      }
+      wg_barrier();
+      // SM2: the rescale of O and the pinned 16-bit P~ (left alone, the compiler would sink
+      // the conversions into the next matrix phase)
+      if constexpr (PH != 2) {
+        if (rs) rescale_o<DT>(O[0], alpha);
+#pragma unroll
+        for (int i = 0; i < KS; ++i) lds_dep(P[i]);
+      }
+      if (grp == 0) {
+        // K(j+1) landed; K(j+2), issued in SM1, may still be in flight
+        if (j + 2 < ntl)
+          wait_vmcnt<LPT>();
+        else
+          wait_vmcnt<0>();
+      }
+      wg_barrier();
+    };
+    const int jm = min(max(kfull[0] - jb, 0), ntl);
+    auto run = [&](auto mask_c, int j0, int j1) __attribute__((always_inline)) {
+      for (int jj = j0 - j0 % 3; jj < j1; jj += 3) {
+        static_for<0, 3>([&](auto st_c) __attribute__((always_inline)) {
+          const int j = jj + decltype(st_c)::value;
+          if (j >= j0 && j < j1) step(st_c, mask_c, IC<1>{}, j);
+        });
+      }
+    };
+    if (ntl > 0) {
+      if (jm > 0)
+        step(IC<0>{}, std::false_type{}, IC<0>{}, 0);
+      else
+        step(IC<0>{}, std::true_type{}, IC<0>{}, 0);
+      run(std::false_type{}, 1, jm);
+      run(std::true_type{}, max(jm, 1), ntl);
+      const int sl = ntl % 3;
+      if (sl == 0)
+        step(IC<0>{}, std::true_type{}, IC<2>{}, ntl);
+      else if (sl == 1)
+        step(IC<1>{}, std::true_type{}, IC<2>{}, ntl);
+      else
+        step(IC<2>{}, std::true_type{}, IC<2>{}, ntl);
+    }
+    // every wavefront passes the same number of barriers
+    if (grp <= 1) wg_barrier();
+    if (grp == 0) wg_barrier();
+    finish(0);
   } else {
     // Ping-pong over two groups of four wavefronts (see the header comment).  Every
     // wavefront runs the same program, step j = MMA(j) | barrier | SM(j) | barrier, where

@@ -10,6 +10,7 @@
 //   schedule 2 (ping-pong of two groups of four wavefronts): B_r 256 x B_c in {32, 64, 128},
 //       3-slot rings;
 //   schedule 4 (three wavefronts per SIMD): B_r in {64, 128} x B_c 32 x stages 2..3;
+//   schedule 5 (three-group rotation, twelve wavefronts): B_r 384 x B_c 32, 3-slot rings;
 // less what does not fit one CU's 160 KB of LDS and what the compiler spills registers
 // for (in_space below).  Each instantiation unit compiles one part of it for one
 // (d_head, dtype).
@@ -81,6 +82,7 @@ void register_part(AddEntryFn add) {
       constexpr int BR = 64 << decltype(ri)::value;
       host_for<2, 4>([&](auto si) { add_if_in_space<D, BR, 32, BR / 32, decltype(si)::value, F16, 4>(add); });
     });
+    add_if_in_space<D, 384, 32, 12, 3, F16, 5>(add);
   }
 }
 

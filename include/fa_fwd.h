@@ -82,7 +82,12 @@ typedef enum {
  *              2 = ping-pong: eight wavefronts of 32 rows in two groups that
  *                  alternate, across a workgroup barrier, between the matrix
  *                  products and the softmax (same page, section 15.3); needs
- *                  waves = 8 and stages = 2 */
+ *                  br = 256, waves = 8 and stages = 3;
+ *              4 = schedule 0 with bc = 32 at three wavefronts per SIMD
+ *                  (waves = br / 32 of 2 or 4, stages 2 or 3);
+ *              5 = three groups of four wavefronts rotating through one
+ *                  matrix phase and two softmax phases across workgroup
+ *                  barriers; needs br = 384, bc = 32, waves = 12, stages = 3 */
 typedef struct {
   int br;
   int bc;

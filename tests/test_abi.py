@@ -87,9 +87,11 @@ def test_config_registry_host_only():
             assert len(cfgs) == fa.fa_fwd_num_configs(d, dtype) >= 1
             for c in cfgs:
                 assert c.stages in (1, 2, 3, 4)
-                assert c.schedule in (0, 1, 2, 4)
-                if c.schedule == 4:
+                assert c.schedule in (0, 1, 2, 4, 5)
+                if c.schedule in (4, 5):
                     assert c.bc == 32
+                if c.schedule == 5:
+                    assert c.br == 384 and c.waves == 12 and c.stages == 3
                 tile = c.bc * d * 2
                 if c.schedule == 1:
                     assert c.br == 64 * c.waves and c.stages == 2

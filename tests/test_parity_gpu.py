@@ -209,9 +209,10 @@ def test_repeat_launches_bitwise_identical():
 
 @pytest.mark.parametrize("ref,alt", [((256, 32, 8, 2, 0), (256, 32, 4, 2, 1)),
                                      ((256, 64, 8, 2, 0), (256, 64, 8, 3, 2)),
-                                     ((128, 32, 4, 2, 0), (128, 32, 4, 2, 4))])
+                                     ((128, 32, 4, 2, 0), (128, 32, 4, 2, 4)),
+                                     ((128, 32, 4, 2, 0), (384, 32, 12, 3, 5))])
 def test_schedules_match_in_order_bitwise_on_ragged_shapes(ref, alt):
-    # The dual-block, ping-pong and three-per-SIMD schedules reorder work inside or across
+    # The dual-block, ping-pong, three-per-SIMD and three-group schedules reorder work inside or across
     # wavefronts, not the arithmetic of a row, so with the same key tile they give the same bits.
     # (1, 2, 3, 16 and 64 key tiles of 64: the ping-pong runs its first and last steps outside
     # the loop, so the shortest streams have no loop step at all)
