@@ -788,9 +788,14 @@ fa_fwd_kernel(FaArgs a) {
     constexpr int STAGE = 2 * TILE;  // K tile then V tile
     constexpr int LPT = 2 * (NCH >= NW ? NCH / NW : 1);  // loads per tile of a loading wavefront
     static_assert(NCH % NW == 0 || NW % NCH == 0, "tile pieces spread evenly");
-    auto step = [&](auto st_c, auto mask_c, int j) __attribute__((always_inline)) {
+    // MODE 0: no masked key in the tile, speculative softmax; 1: the tile may hold masked
+    // keys; 2: no masked key, and the tile is the workgroup's first (m is still -inf, so the
+    // speculation would fail and the exponentials be taken twice; O is still zero, so its
+    // rescale by alpha = 0 is left out).
+    auto step = [&](auto st_c, auto mode_c, int j) __attribute__((always_inline)) {
       constexpr int ST = decltype(st_c)::value;
-      constexpr bool MK = decltype(mask_c)::value;
+      constexpr int MODE = decltype(mode_c)::value;
+      constexpr bool MK = MODE == 1;
       if constexpr (STAGES == 1) {
         if (j > 0) {
           __syncthreads();  // everyone is done with tile j-1
@@ -833,10 +838,10 @@ fa_fwd_kernel(FaArgs a) {
         qk_block<D, BC, F16, QK_LA, IMM ? SO : 0>(base, S, qreg[0], ad);
         // (schedule 4 keeps the plain step: the speculative one's extra registers spill there)
         const float alpha =
-            MK || SCHED == 4
+            MODE != 0 || SCHED == 4
                 ? softmax_block<BC, F16, MK>(S, P, m[0], l[0], c, MK ? klim[0] - (jb + j) * BC - 4 * hi : 0, rs)
                 : softmax_block_spec<BC, F16>(S, P, m[0], l[0], c, rs);
-        if (rs) rescale_o<DT>(O[0], alpha);
+        if (MODE != 2 && rs) rescale_o<DT>(O[0], alpha);
         pv_block<D, BC, F16, PV_LA, (IMM ? SO : 0) + TILE>(base, P, O[0], ad);
       }
     };
@@ -845,11 +850,11 @@ fa_fwd_kernel(FaArgs a) {
     // (or, with the branch around the whole tile, the output accumulators) of the two paths
     // meet at the end of every step and the compiler copies all of them between registers.
     const int jm = min(max(kfull[0] - jb, 0), ntl);
-    auto run = [&](auto mask_c, int j0, int j1) __attribute__((always_inline)) {
+    auto run = [&](auto mode_c, int j0, int j1) __attribute__((always_inline)) {
       for (int jj = j0 - j0 % STAGES; jj < j1; jj += STAGES) {
         static_for<0, STAGES>([&](auto st_c) __attribute__((always_inline)) {
           const int j = jj + decltype(st_c)::value;
-          if (j >= j0 && j < j1) step(st_c, mask_c, j);
+          if (j >= j0 && j < j1) step(st_c, mode_c, j);
         });
       }
     };
@@ -860,8 +865,13 @@ fa_fwd_kernel(FaArgs a) {
         load_one(vb, smem + t * STAGE + TILE, jb + t);
       }
     }
-    run(std::false_type{}, 0, jm);
-    run(std::true_type{}, jm, ntl);
+    if constexpr (SCHED == 4) {
+      run(IC<0>{}, 0, jm);  // (no speculation to spare; a separate first step spills)
+    } else if (jm > 0) {
+      step(IC<0>{}, IC<2>{}, 0);
+      run(IC<0>{}, 1, jm);
+    }
+    run(IC<1>{}, jm, ntl);
     finish(0);
   } else if constexpr (SCHED == 1) {
     // Dual-block software pipeline (see the header comment).  Step j:
@@ -964,8 +974,10 @@ fa_fwd_kernel(FaArgs a) {
         if (j + 1 < ntl) load_by(vb, smem + SN * TILE, jb + j + 1, gw, Four{});
       }
       if constexpr (PH != 2) {
-        alpha = MK ? softmax_block<BC, F16, true>(S, P, m[0], l[0], c, klim[0] - (jb + j) * BC - 4 * hi, rs)
-                   : softmax_block_spec<BC, F16>(S, P, m[0], l[0], c, rs);
+        // (step 0: m is still -inf, the speculation would fail)
+        alpha = MK || PH == 0
+                    ? softmax_block<BC, F16, MK>(S, P, m[0], l[0], c, MK ? klim[0] - (jb + j) * BC - 4 * hi : 0, rs)
+                    : softmax_block_spec<BC, F16>(S, P, m[0], l[0], c, rs);
         lds_dep(l[0]);
       }
       if (grp == 1) {
@@ -979,7 +991,7 @@ fa_fwd_kernel(FaArgs a) {
       // SM2: the rescale of O and the pinned 16-bit P~ (left alone, the compiler would sink
       // the conversions into the next matrix phase)
       if constexpr (PH != 2) {
-        if (rs) rescale_o<DT>(O[0], alpha);
+        if (PH != 0 && rs) rescale_o<DT>(O[0], alpha);  // (O is still zero at step 0)
 #pragma unroll
         for (int i = 0; i < KS; ++i) lds_dep(P[i]);
       }
@@ -1075,10 +1087,13 @@ fa_fwd_kernel(FaArgs a) {
       }
       if constexpr (PH != 2) {
         bool rs;
+        // (step 0: m is still -inf, so the speculation would fail, and O is still zero, so
+        // its rescale by alpha = 0 is left out)
         const float alpha =
-            MK ? softmax_block<BC, F16, true>(S, P, m[0], l[0], c, klim[0] - (jb + j) * BC - 4 * hi, rs)
-               : softmax_block_spec<BC, F16>(S, P, m[0], l[0], c, rs);
-        if (rs) rescale_o<DT>(O[0], alpha);
+            MK || PH == 0
+                ? softmax_block<BC, F16, MK>(S, P, m[0], l[0], c, MK ? klim[0] - (jb + j) * BC - 4 * hi : 0, rs)
+                : softmax_block_spec<BC, F16>(S, P, m[0], l[0], c, rs);
+        if (PH != 0 && rs) rescale_o<DT>(O[0], alpha);
         // The 16-bit P~ and the running sum are formed here, in the softmax half: left to
         // itself the compiler sank their conversions past the barrier, into the start of
         // the next matrix half, ahead of its first LDS reads.
