@@ -116,10 +116,10 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload):
+def read_traffic(workload, cfg, splits):
     """HBM bytes per launch from the committed rocprofv3 counter summary
     (profiles/fa_fwd_<workload>_traffic.txt, "key: value" lines), if it was taken on the
-    current kernel sources; else None."""
+    current kernel sources with the same tile configuration and split count; else None."""
     path = os.path.join(ROOT, "profiles", "fa_fwd_%s_traffic.txt" % workload)
     vals = {}
     try:
@@ -132,6 +132,8 @@ def read_traffic(workload):
     except OSError:
         return None
     if vals.get("kernel_source_hash") != kernel_source_hash() or vals.get("workload") != workload:
+        return None
+    if vals.get("tile") != ",".join(str(x) for x in cfg.as_tuple()) or vals.get("num_splits") != str(splits):
         return None
     try:
         return int(float(vals["hbm_bytes_per_launch"]))
@@ -198,8 +200,9 @@ def setup(name, dev, splits=0, which="fwd", atomic_dq=False, tune=True, tune_rou
     With tune, the library's autotuner first times every compiled tile configuration on these
     buffers (fa_fwd_autotune_ext, interleaved median timing) and the step then runs its pick.
     The parity tests launch through this same function.  Returns a dict with w (the workload),
-    o, lse, step, cfg (the forward tile configuration), splits, tuned (the tuner's report or
-    None), flops, nbytes, stream and desc."""
+    o, lse, step, cfg (the forward tile configuration), source (where the library took it from:
+    default, tuned, FA_FWD_CONFIG or forced), splits, tuned (the tuner's report or None), flops,
+    nbytes, stream and desc."""
     import torch
 
     from exact_attention_17_amd import fa, inputs, metrics
@@ -251,8 +254,8 @@ def setup(name, dev, splits=0, which="fwd", atomic_dq=False, tune=True, tune_rou
         fa.fa_fwd_ext(qd, kd, vd, o, lse, scale=w["scale"], causal=causal, cu_seqlens=cu,
                       max_seqlen=w["max_seqlen"], num_splits=req_splits, workspace=workspace, stream=stream)
 
-    out = dict(w=w, o=o, lse=lse, step=step, cfg=cfg, splits=splits, tuned=tuned, flops=flops, nbytes=nbytes,
-               stream=stream, desc="fa_fwd_ext tiles %r (%s), %d split(s)" % (cfg, source, splits))
+    out = dict(w=w, o=o, lse=lse, step=step, cfg=cfg, source=source, splits=splits, tuned=tuned, flops=flops,
+               nbytes=nbytes, stream=stream, desc="fa_fwd_ext tiles %r (%s), %d split(s)" % (cfg, source, splits))
     if which == "bwd":
         step()  # O and LSE of this workload
         g = torch.Generator().manual_seed(int(w["seed"]) + 1000)
@@ -338,7 +341,7 @@ def main():
         % (args.workload, args.which, ms, wall * 1e3 / args.steps, tflops, 100 * tflops / PEAK_BF16_TFLOPS,
            PEAK_BF16_TFLOPS, cfg, splits))
 
-    traffic = read_traffic(args.workload) if args.which == "fwd" else None
+    traffic = read_traffic(args.workload, cfg, splits) if args.which == "fwd" else None
     cpu = None
     if not args.no_cpu_baseline and args.which == "fwd":
         log("timing the fp64 oracle on a bounded sample")
@@ -365,7 +368,8 @@ def main():
         "config": {"workload": wl, "batch": w["batch"], "seq_len_q": w["seqlen_q"], "seq_len_k": w["seqlen_k"],
                    "heads": w["heads"], "heads_kv": hkv, "d_head": w["d_head"], "causal": causal,
                    "tile": ({"br": cfg.br, "bc": cfg.bc, "waves": cfg.waves, "stages": cfg.stages,
-                             "schedule": cfg.schedule, "tuned": bool(st["tuned"])} if args.which == "fwd" else
+                             "schedule": cfg.schedule, "tuned": st["source"] == "tuned", "source": st["source"]}
+                            if args.which == "fwd" else
                             {"dkdv_keys_per_workgroup": 64 if w["d_head"] == 32 else 128,
                              "dq_pass_rows_per_workgroup": 256 if w["d_head"] == 128 else 128}),
                    "num_splits": splits, "pass": args.which,

@@ -6,6 +6,7 @@ import subprocess
 import sys
 
 import bench
+from exact_attention_17_amd import fa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -41,14 +42,18 @@ def test_traffic_is_read_only_for_the_current_kernel(tmp_path, monkeypatch):
     (tmp_path / "profiles").mkdir()
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     h = bench.kernel_source_hash()
+    cfg = fa.TileConfig(256, 64, 8, 3, 2)
+    tail = "tile: 256,64,8,3,2\nnum_splits: 1\nhbm_bytes_per_launch: 1234\n"
     prof = tmp_path / "profiles" / "fa_fwd_full_traffic.txt"
-    prof.write_text("# header: ignored\nworkload: full\nkernel_source_hash: %s\nhbm_bytes_per_launch: 1234\n" % h)
-    assert bench.read_traffic("full") == 1234
-    assert bench.read_traffic("varlen") is None  # no such profile
-    prof.write_text("workload: full\nkernel_source_hash: 0000000000000000\nhbm_bytes_per_launch: 1234\n")
-    assert bench.read_traffic("full") is None  # taken on other kernel sources
-    prof.write_text("workload: gqa\nkernel_source_hash: %s\nhbm_bytes_per_launch: 1234\n" % h)
-    assert bench.read_traffic("full") is None  # another workload's numbers
+    prof.write_text("# header: ignored\nworkload: full\nkernel_source_hash: %s\n%s" % (h, tail))
+    assert bench.read_traffic("full", cfg, 1) == 1234
+    assert bench.read_traffic("varlen", cfg, 1) is None  # no such profile
+    assert bench.read_traffic("full", fa.TileConfig(128, 32, 4, 2, 4), 1) is None  # another tile's numbers
+    assert bench.read_traffic("full", cfg, 4) is None  # another split count's
+    prof.write_text("workload: full\nkernel_source_hash: 0000000000000000\n" + tail)
+    assert bench.read_traffic("full", cfg, 1) is None  # taken on other kernel sources
+    prof.write_text("workload: gqa\nkernel_source_hash: %s\n%s" % (h, tail))
+    assert bench.read_traffic("full", cfg, 1) is None  # another workload's numbers
 
 
 def test_committed_traffic_summaries_are_consistent():
@@ -67,3 +72,4 @@ def test_committed_traffic_summaries_are_consistent():
         assert int(vals["hbm_bytes_per_launch"]) == int(vals["fetch_bytes_per_launch"]) + int(
             vals["write_bytes_per_launch"])
         assert len(vals["kernel_source_hash"]) == 16
+        assert len(vals["tile"].split(",")) == 5 and int(vals["num_splits"]) >= 1
