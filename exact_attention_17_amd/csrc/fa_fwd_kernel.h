@@ -517,6 +517,63 @@ __device__ __forceinline__ float softmax_block_spec(const f32x16 (&S)[BC / 32], 
   return alpha;
 }
 
+// The speculative step without a second copy of the scores, for schedules whose registers
+// cannot hold one: the exponentials overwrite S.  When the partial-sum test fails (always on
+// a row's first tile, where m = -inf makes the sum +inf), `rescore` forms the scores again
+// from the K tile still in LDS and the step continues as the plain one.  The result is the
+// plain step's, bit for bit, as for softmax_block_spec.
+template <int BC, bool F16, typename Rescore>
+__device__ __forceinline__ float softmax_block_spec_inplace(f32x16 (&S)[BC / 32], i32x4 (&P)[BC / 16], float &m,
+                                                            float &l, float c, bool &rescale, Rescore &&rescore) {
+  constexpr int KB = BC / 32;
+  float mc = m * c;
+  RowSum<KB> part;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      S[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], c, -mc));
+      part.add(16 * kb + r, S[kb][r]);
+    }
+  float rs = part.total();
+  float alpha = 1.f;
+  rescale = false;
+  if (__builtin_amdgcn_ballot_w64(!(rs <= kLazyBound)) != 0) {
+    rescore(S);
+    float mx = S[0][0];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
+    mx = pair_max(mx);
+    const bool grow = (mx - m) * c > kLazyRescale;
+    const float m_new = grow ? mx : m;
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    alpha = __builtin_amdgcn_exp2f((m - m_ref) * c);
+    rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
+    m = m_new;
+    mc = m_ref * c;
+    RowSum<KB> again;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        S[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], c, -mc));
+        again.add(16 * kb + r, S[kb][r]);
+      }
+    rs = again.total();
+  }
+  l = l * alpha + rs;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        P[2 * kb + s2][e] = pack2<F16>(S[kb][8 * s2 + 2 * e], S[kb][8 * s2 + 2 * e + 1]);
+  return alpha;
+}
+
 template <int DT>
 __device__ __forceinline__ void rescale_o(f32x16 (&O)[DT], float alpha) {
 #pragma unroll
@@ -836,11 +893,14 @@ fa_fwd_kernel(FaArgs a) {
         constexpr bool IMM = SO + STAGE <= 65536;
         const char *base = IMM ? smem : smem + SO;
         qk_block<D, BC, F16, QK_LA, IMM ? SO : 0>(base, S, qreg[0], ad);
-        // (schedule 4 keeps the plain step: the speculative one's extra registers spill there)
+        // (schedule 4 speculates in place: a second copy of the scores spills there)
+        auto rescore = [&](f32x16(&S2)[KB]) __attribute__((always_inline)) {
+          qk_block<D, BC, F16, QK_LA, IMM ? SO : 0>(base, S2, qreg[0], ad);
+        };
         const float alpha =
-            MODE != 0 || SCHED == 4
-                ? softmax_block<BC, F16, MK>(S, P, m[0], l[0], c, MK ? klim[0] - (jb + j) * BC - 4 * hi : 0, rs)
-                : softmax_block_spec<BC, F16>(S, P, m[0], l[0], c, rs);
+            MODE != 0 ? softmax_block<BC, F16, MK>(S, P, m[0], l[0], c, MK ? klim[0] - (jb + j) * BC - 4 * hi : 0, rs)
+            : SCHED == 4 ? softmax_block_spec_inplace<BC, F16>(S, P, m[0], l[0], c, rs, rescore)
+                         : softmax_block_spec<BC, F16>(S, P, m[0], l[0], c, rs);
         if (MODE != 2 && rs) rescale_o<DT>(O[0], alpha);
         pv_block<D, BC, F16, PV_LA, (IMM ? SO : 0) + TILE>(base, P, O[0], ad);
       }
@@ -865,9 +925,7 @@ fa_fwd_kernel(FaArgs a) {
         load_one(vb, smem + t * STAGE + TILE, jb + t);
       }
     }
-    if constexpr (SCHED == 4) {
-      run(IC<0>{}, 0, jm);  // (no speculation to spare; a separate first step spills)
-    } else if (jm > 0) {
+    if (jm > 0) {
       step(IC<0>{}, IC<2>{}, 0);
       run(IC<0>{}, 1, jm);
     }
