@@ -379,14 +379,12 @@ __device__ __forceinline__ void pvqk_block(const char *sv, const i32x4 (&P)[BC /
 }
 
 // A lane's share of a row sum over one tile, term i being accumulator register i % 16 of
-// 32-key block i / 16.  With 64 or more keys per tile (32 or more terms per lane) it is
-// accumulated in four interleaved partial sums (term i goes to sum i % 4), added pairwise at
-// the end: four short chains of dependent adds instead of one long one (about 0.5 % on the
-// ping-pong schedule).  With 32-key tiles it is one chain: the three-wavefront-per-SIMD
-// schedule ran 0.7 % slower with four.
-template <int KB>
+// 32-key block i / 16.  It is accumulated in four interleaved partial sums (term i goes to
+// sum i % 4), added pairwise at the end: four short chains of dependent adds instead of one
+// long one (about 0.5 % on the ping-pong schedule; on 32-key tiles 0.6 % under the causal
+// mask and 0.8-1.4 % at d_head 32).
 struct RowSum {
-  static constexpr int NP = KB >= 2 ? 4 : 1;
+  static constexpr int NP = 4;
   float v[NP];
   // the first NP terms start the sums (0 + x is x exactly for these terms, all >= 0)
   __device__ __forceinline__ void add(int i, float x) {
@@ -395,10 +393,7 @@ struct RowSum {
     else
       v[i % NP] += x;
   }
-  __device__ __forceinline__ float total() const {
-    if constexpr (NP == 4) return (v[0] + v[1]) + (v[2] + v[3]);
-    return v[0];
-  }
+  __device__ __forceinline__ float total() const { return (v[0] + v[1]) + (v[2] + v[3]); }
 };
 
 // Online softmax step of one 32-query block on the raw scores S of tile j (keys from
@@ -437,7 +432,7 @@ __device__ __forceinline__ float softmax_block(f32x16 (&S)[BC / 32], i32x4 (&P)[
   rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
   m = m_new;
   const float mc = m_ref * c;
-  RowSum<KB> rs;
+  RowSum rs;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -471,7 +466,7 @@ __device__ __forceinline__ float softmax_block_spec(const f32x16 (&S)[BC / 32], 
   constexpr int KB = BC / 32;
   f32x16 E[KB];
   float mc = m * c;
-  RowSum<KB> part;
+  RowSum part;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -496,7 +491,7 @@ __device__ __forceinline__ float softmax_block_spec(const f32x16 (&S)[BC / 32], 
     rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
     m = m_new;
     mc = m_ref * c;
-    RowSum<KB> again;
+    RowSum again;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -527,7 +522,7 @@ __device__ __forceinline__ float softmax_block_spec_inplace(f32x16 (&S)[BC / 32]
                                                             float &l, float c, bool &rescale, Rescore &&rescore) {
   constexpr int KB = BC / 32;
   float mc = m * c;
-  RowSum<KB> part;
+  RowSum part;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -553,7 +548,7 @@ __device__ __forceinline__ float softmax_block_spec_inplace(f32x16 (&S)[BC / 32]
     rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
     m = m_new;
     mc = m_ref * c;
-    RowSum<KB> again;
+    RowSum again;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
