@@ -378,7 +378,10 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "algorithmic_bytes": nbytes,
-                     "algorithmic_flops": flops},
+                     "algorithmic_flops": flops,
+                     # the HBM roofline beside it: algorithmic bytes per launch over its time
+                     "hbm_achieved_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "cpu_baseline": cpu,
         "tuning": st["tuned"],
         "launch_ms": {"median": round(per_launch[len(per_launch) // 2], 5), "min": round(per_launch[0], 5)},
