@@ -291,6 +291,11 @@ FaArgs make_args(const void *q, const void *k, const void *v, void *o, float *ls
   a.num_splits = num_splits;
   a.n_qtiles = (seqlen_q + br - 1) / br;
   a.total_wgs = batch * n_heads * a.n_qtiles * num_splits;
+  a.div_splits = fa::make_fastdiv((uint32_t)num_splits);
+  a.div_qtiles = fa::make_fastdiv((uint32_t)a.n_qtiles);
+  a.div_group = fa::make_fastdiv((uint32_t)a.group);
+  a.div_heads_kv = fa::make_fastdiv((uint32_t)n_heads_kv);
+  a.div_batch = fa::make_fastdiv((uint32_t)batch);
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
   a.o_part = o_part;
   a.lse_part = lse_part;

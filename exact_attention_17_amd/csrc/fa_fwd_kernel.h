@@ -689,26 +689,28 @@ fa_fwd_kernel(FaArgs a) {
   const int G = a.total_wgs;
   const int per = G >> 3, rem = G & 7, xcd = w & 7;
   const int lin = xcd * per + min(xcd, rem) + (w >> 3);
+  // (divisions by the launch's fixed divisors: multiply-high, add, shift)
   const int nsplit = a.num_splits;
-  const int split = lin % nsplit;
-  const int lt = lin / nsplit;
-  const int qi = lt % a.n_qtiles;
+  const int lt = (int)fast_div((uint32_t)lin, a.div_splits);
+  const int split = lin - lt * nsplit;
+  const int ght = (int)fast_div((uint32_t)lt, a.div_qtiles);
+  const int qi = lt - ght * a.n_qtiles;
   // under the causal mask the work of a query tile grows with its index: start the longest
   const int qt = a.causal ? a.n_qtiles - 1 - qi : qi;
   // head-major: an XCD's contiguous range covers a few K/V heads of every sequence, so packed
   // sequences of different lengths spread evenly over the XCDs, while the query tiles of one
   // (sequence, K/V head) -- of all the query heads that share it -- stay together and share
   // that XCD's L2 for their K/V.  Order: (K/V head, sequence, head in group, query tile).
-  const int ght = lt / a.n_qtiles;
-  const int gi = ght % a.group;
-  const int hkb = ght / a.group;
+  const int hkb = (int)fast_div((uint32_t)ght, a.div_group);
+  const int gi = ght - hkb * a.group;
   // Dense calls whose head rows are under 128 bytes (d_head 32) take the sequence outermost
   // instead, so that the heads sharing a cache line of a token row are read by workgroups
   // running at the same time (2.5 % on B64 N512 H16 d32, which fetches about twice its
   // input bytes from HBM).
   const bool seq_major = D * 2 < 128 && !a.cu_seqlens;
-  const int b = seq_major ? hkb / a.heads_kv : hkb % a.batch;
-  const int hk = seq_major ? hkb % a.heads_kv : hkb / a.batch;  // the K/V head this query head reads
+  const int hkq = (int)fast_div((uint32_t)hkb, seq_major ? a.div_heads_kv : a.div_batch);
+  const int b = seq_major ? hkq : hkb - hkq * a.batch;
+  const int hk = seq_major ? hkb - hkq * a.heads_kv : hkq;  // the K/V head this query head reads
   const int h = hk * a.group + gi;
 
   int nq, nk;
@@ -750,8 +752,8 @@ fa_fwd_kernel(FaArgs a) {
   // `split` of nsplit takes tiles [jb, je) of them.
   const int kend = a.causal ? min(nk, q_tile0 + BR) : nk;
   const int nkt_all = (kend + BC - 1) / BC;
-  const int jb = (int)((int64_t)nkt_all * split / nsplit);
-  const int je = (int)((int64_t)nkt_all * (split + 1) / nsplit);
+  const int jb = nsplit == 1 ? 0 : (int)((int64_t)nkt_all * split / nsplit);
+  const int je = nsplit == 1 ? nkt_all : (int)((int64_t)nkt_all * (split + 1) / nsplit);
   const int ntl = je - jb;  // may be 0: the split then reports "no visible key"
 
   // Q stays in registers as the B operand (16 d per step) of each 32-row block.

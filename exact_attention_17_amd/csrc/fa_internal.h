@@ -7,6 +7,31 @@
 
 namespace fa {
 
+// Division by a divisor fixed for the whole launch, as a multiply-high, an add and a shift
+// (division by invariant integers using multiplication, after Granlund and Montgomery): with
+// shift = ceil(log2 d) and mul = floor(2^32 (2^shift - d) / d) + 1, n / d equals
+// (mulhi(n, mul) + n) >> shift for every 0 <= n < 2^32; for n < 2^31 the sum cannot overflow
+// 32 bits.  It replaces the kernels' work-item decoding by integer division, which the
+// compiler expands to a few dozen scalar instructions per division.
+struct FastDiv {
+  uint32_t d;
+  uint32_t mul;
+  uint32_t shift;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  const uint32_t shift = d <= 1 ? 0 : 32 - (uint32_t)__builtin_clz(d - 1);  // ceil(log2 d)
+  const uint64_t mul = ((uint64_t(1) << 32) * ((uint64_t(1) << shift) - d)) / d + 1;
+  return FastDiv{d, (uint32_t)mul, shift};
+}
+
+// n / f.d for 0 <= n < 2^31.
+// (The high half of the 64-bit product compiles to one multiply-high instruction.)
+__host__ __device__ inline uint32_t fast_div(uint32_t n, const FastDiv &f) {
+  const uint32_t hi = (uint32_t)(((uint64_t)n * f.mul) >> 32);
+  return (hi + n) >> f.shift;
+}
+
 // Kernel arguments, passed by value.
 struct FaArgs {
   const void *q;
@@ -25,6 +50,8 @@ struct FaArgs {
   int num_splits;  // key tiles of each query tile are divided among this many workgroups
   int n_qtiles;    // ceil(seqlen_q / br)
   int total_wgs;   // batch * heads * n_qtiles * num_splits
+  // the divisors of the work-item decoding
+  FastDiv div_splits, div_qtiles, div_group, div_heads_kv, div_batch;
   float scale_log2;  // scale * log2(e): scores go through exp2
   // num_splits > 1: each workgroup writes its split's normalised fp32 output and natural-log
   // LSE here instead of o / lse; the merge kernel combines them.
