@@ -1126,12 +1126,20 @@ fa_fwd_kernel(FaArgs a) {
       constexpr int PH = decltype(ph_c)::value;
       constexpr int SP = (ST + 2) % 3;  // slot of tile j - 1 (and of tile j + 2)
       constexpr int SN = (ST + 1) % 3;  // slot of tile j + 1
+      // A slot's offset rides in the reads' 16-bit immediate field when the farthest read of
+      // the tile still fits; otherwise (96-key tiles, third slot) the slot goes into the base
+      // address and the per-lane addresses are formed again for it.
+      constexpr bool VI = SP * TILE + 16 * (KS - 1) * ROWB < 65536;
+      constexpr bool KI = ST * TILE + (KB - 1) * 32 * ROWB < 65536;
+      constexpr int VO = VI ? SP * TILE : 0, KO = KI ? ST * TILE : 0;
+      const char *const vsl = VI ? smem : smem + SP * TILE;
+      const char *const ksl = KI ? kbase : kbase + ST * TILE;
       if constexpr (PH == 1) {
-        pvqk_block<D, BC, F16, 5, SP * TILE, ST * TILE>(smem, P, O[0], kbase, S, qreg[0], ad);
+        pvqk_block<D, BC, F16, 5, VO, KO>(vsl, P, O[0], ksl, S, qreg[0], ad);
       } else if constexpr (PH == 0) {
-        qk_block<D, BC, F16, 6, ST * TILE>(kbase, S, qreg[0], ad);
+        qk_block<D, BC, F16, 6, KO>(ksl, S, qreg[0], ad);
       } else {
-        pv_block<D, BC, F16, 4, SP * TILE>(smem, P, O[0], ad);
+        pv_block<D, BC, F16, 4, VO>(vsl, P, O[0], ad);
       }
       if (grp == 1) wait_vmcnt<0>();  // V(j), issued in the previous step, landed
       wg_barrier();
@@ -1144,10 +1152,15 @@ fa_fwd_kernel(FaArgs a) {
         bool rs;
         // (step 0: m is still -inf, so the speculation would fail, and O is still zero, so
         // its rescale by alpha = 0 is left out)
+        // (speculation in place: the K tile of this step is still in its slot, so the scores
+        // can be formed again if the test fails)
+        auto rescore = [&](f32x16(&S2)[KB]) __attribute__((always_inline)) {
+          qk_block<D, BC, F16, 6, KO>(ksl, S2, qreg[0], ad);
+        };
         const float alpha =
             MK || PH == 0
                 ? softmax_block<BC, F16, MK>(S, P, m[0], l[0], c, MK ? klim[0] - (jb + j) * BC - 4 * hi : 0, rs)
-                : softmax_block_spec<BC, F16>(S, P, m[0], l[0], c, rs);
+                : softmax_block_spec_inplace<BC, F16>(S, P, m[0], l[0], c, rs, rescore);
         if (PH != 0 && rs) rescale_o<DT>(O[0], alpha);
         // The 16-bit P~ and the running sum are formed here, in the softmax half: left to
         // itself the compiler sank their conversions past the barrier, into the start of

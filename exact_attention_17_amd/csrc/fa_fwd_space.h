@@ -7,8 +7,8 @@
 //       x B_c in {32, 64, 128} x stages 1..4;
 //   schedule 1 (two 32-row blocks per wavefront, one wavefront per SIMD): B_r in {64, 128,
 //       256} (1, 2, 4 wavefronts) x B_c in {32, 64, 128}, a 2-slot K and 3-slot V ring;
-//   schedule 2 (ping-pong of two groups of four wavefronts): B_r 256 x B_c in {32, 64, 128},
-//       3-slot rings;
+//   schedule 2 (ping-pong of two groups of four wavefronts): B_r 256 x B_c in {32, 64, 128}
+//       and, at d_head 64 and 128, 96, 3-slot rings;
 //   schedule 4 (three wavefronts per SIMD): B_r in {64, 128} x B_c 32 x stages 2..3;
 //   schedule 5 (three-group rotation, twelve wavefronts): B_r 384 x B_c 32, 3-slot rings;
 // less what does not fit one CU's 160 KB of LDS and what the compiler spills registers
@@ -78,6 +78,7 @@ void register_part(AddEntryFn add) {
       host_for<0, 3>([&](auto bi) { add_if_in_space<D, BR, 32 << decltype(bi)::value, BR / 64, 2, F16, 1>(add); });
     });
     host_for<0, 3>([&](auto bi) { add_if_in_space<D, 256, 32 << decltype(bi)::value, 8, 3, F16, 2>(add); });
+    if constexpr (D >= 64) add_if_in_space<D, 256, 96, 8, 3, F16, 2>(add);  // (whole 1 KB pieces)
     host_for<0, 2>([&](auto ri) {
       constexpr int BR = 64 << decltype(ri)::value;
       host_for<2, 4>([&](auto si) { add_if_in_space<D, BR, 32, BR / 32, decltype(si)::value, F16, 4>(add); });
