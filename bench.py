@@ -117,28 +117,33 @@ def kernel_source_hash():
 
 
 def read_traffic(workload, cfg, splits):
-    """HBM bytes per launch from the committed rocprofv3 counter summary
-    (profiles/fa_fwd_<workload>_traffic.txt, "key: value" lines), if it was taken on the
-    current kernel sources with the same tile configuration and split count; else None."""
-    path = os.path.join(ROOT, "profiles", "fa_fwd_%s_traffic.txt" % workload)
-    vals = {}
-    try:
-        with open(path) as f:
-            for line in f:
-                if line.startswith("#") or ":" not in line:
-                    continue
-                key, val = line.split(":", 1)
-                vals[key.strip()] = val.strip()
-    except OSError:
-        return None
-    if vals.get("kernel_source_hash") != kernel_source_hash() or vals.get("workload") != workload:
-        return None
-    if vals.get("tile") != ",".join(str(x) for x in cfg.as_tuple()) or vals.get("num_splits") != str(splits):
-        return None
-    try:
-        return int(float(vals["hbm_bytes_per_launch"]))
-    except (KeyError, ValueError):
-        return None
+    """HBM bytes per launch from a committed rocprofv3 counter summary of the workload
+    (profiles/fa_fwd_<workload>_traffic.txt for the tile the tuner picked when it was taken,
+    profiles/fa_fwd_<workload>_<tile>_traffic.txt for other tiles; "key: value" lines): the one
+    taken on the current kernel sources with this tile configuration and split count, else None."""
+    tile = ",".join(str(x) for x in cfg.as_tuple())
+    paths = [os.path.join(ROOT, "profiles", "fa_fwd_%s_traffic.txt" % workload),
+             os.path.join(ROOT, "profiles", "fa_fwd_%s_%s_traffic.txt" % (workload, tile.replace(",", "-")))]
+    for path in paths:
+        vals = {}
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.startswith("#") or ":" not in line:
+                        continue
+                    key, val = line.split(":", 1)
+                    vals[key.strip()] = val.strip()
+        except OSError:
+            continue
+        if vals.get("kernel_source_hash") != kernel_source_hash() or vals.get("workload") != workload:
+            continue
+        if vals.get("tile") != tile or vals.get("num_splits") != str(splits):
+            continue
+        try:
+            return int(float(vals["hbm_bytes_per_launch"]))
+        except (KeyError, ValueError):
+            continue
+    return None
 
 
 def copy_calibration(nbytes, reps):

@@ -54,6 +54,14 @@ def test_traffic_is_read_only_for_the_current_kernel(tmp_path, monkeypatch):
     assert bench.read_traffic("full", cfg, 1) is None  # taken on other kernel sources
     prof.write_text("workload: gqa\nkernel_source_hash: %s\n%s" % (h, tail))
     assert bench.read_traffic("full", cfg, 1) is None  # another workload's numbers
+    # a second tile's summary, named for its tile
+    prof.write_text("workload: full\nkernel_source_hash: %s\n%s" % (h, tail))
+    alt = tmp_path / "profiles" / "fa_fwd_full_256-96-8-3-2_traffic.txt"
+    alt.write_text("workload: full\nkernel_source_hash: %s\ntile: 256,96,8,3,2\nnum_splits: 1\n"
+                   "hbm_bytes_per_launch: 999\n" % h)
+    assert bench.read_traffic("full", cfg, 1) == 1234
+    assert bench.read_traffic("full", fa.TileConfig(256, 96, 8, 3, 2), 1) == 999
+    assert bench.read_traffic("full", fa.TileConfig(256, 32, 8, 3, 2), 1) is None
 
 
 def test_committed_traffic_summaries_are_consistent():
@@ -68,7 +76,8 @@ def test_committed_traffic_summaries_are_consistent():
                 key, val = line.split(":", 1)
                 vals[key.strip()] = val.strip()
         name = os.path.basename(p)[len("fa_fwd_"):-len("_traffic.txt")]
-        assert vals["workload"] == name
+        # fa_fwd_<workload>_traffic.txt, or fa_fwd_<workload>_<tile>_traffic.txt for another tile
+        assert name == vals["workload"] or name == vals["workload"] + "_" + vals["tile"].replace(",", "-")
         assert int(vals["hbm_bytes_per_launch"]) == int(vals["fetch_bytes_per_launch"]) + int(
             vals["write_bytes_per_launch"])
         assert len(vals["kernel_source_hash"]) == 16
