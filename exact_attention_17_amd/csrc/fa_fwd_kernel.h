@@ -1116,13 +1116,10 @@ fa_fwd_kernel(FaArgs a) {
     wg_barrier();
     if (grp == 1) wg_barrier();
     // Step j in slot ST = j % 3 (a compile-time index, so that slot offsets are immediates).
-    // Phase PH: 0 for step 0 (QK^T only), 1 for steps 1 .. wl (PV and QK^T as one MFMA
-    // stream), 2 for step wl + 1 (PV only), 3 for the steps after it (no work of this
-    // wavefront: only its share of the loads and the barriers), where wl is the wavefront's
-    // last tile with a visible key (ntl - 1 unless the causal mask hides the later tiles from
-    // all of its rows).  The first and last working steps run outside the loops, so that the
-    // loop body has no branch around its matrix products (with one, the registers of both
-    // paths met at the join and the kernel spilled).
+    // Phase PH: 0 for step 0 (QK^T only), 1 for steps 1 .. ntl-1 (PV and QK^T as one MFMA
+    // stream), 2 for step ntl (PV only).  The first and last steps run outside the loops, so
+    // that the loop body has no branch around its matrix products (with one, the registers
+    // of both paths met at the join and the kernel spilled).
     auto step = [&](auto st_c, auto mask_c, auto ph_c, int j) __attribute__((always_inline)) {
       constexpr int ST = decltype(st_c)::value;
       constexpr bool MK = decltype(mask_c)::value;
@@ -1141,7 +1138,7 @@ fa_fwd_kernel(FaArgs a) {
         pvqk_block<D, BC, F16, 5, VO, KO>(vsl, P, O[0], ksl, S, qreg[0], ad);
       } else if constexpr (PH == 0) {
         qk_block<D, BC, F16, 6, KO>(ksl, S, qreg[0], ad);
-      } else if constexpr (PH == 2) {
+      } else {
         pv_block<D, BC, F16, 4, VO>(vsl, P, O[0], ad);
       }
       if (grp == 1) wait_vmcnt<0>();  // V(j), issued in the previous step, landed
@@ -1151,7 +1148,7 @@ fa_fwd_kernel(FaArgs a) {
       } else {
         if (j + 1 < ntl) load_by(vb, smem + SN * TILE, jb + j + 1, gw, Four{});
       }
-      if constexpr (PH < 2) {
+      if constexpr (PH != 2) {
         bool rs;
         // (step 0: m is still -inf, so the speculation would fail, and O is still zero, so
         // its rescale by alpha = 0 is left out)
@@ -1185,36 +1182,29 @@ fa_fwd_kernel(FaArgs a) {
     // a loop of its own, as in schedule 0.  With no tile at all (an empty split) there is no
     // step; both groups still pass the same number of barriers.
     const int jm = min(max(kfull[0] - jb, 0), ntl);
-    // (-1 when none of this split's tiles has a key visible to the wavefront)
-    const int wl = max(-1, min(ntl - 1, (wave_kend - 1) / BC - jb));
-    auto run = [&](auto mask_c, auto ph_c, int j0, int j1) __attribute__((always_inline)) {
+    auto run = [&](auto mask_c, int j0, int j1) __attribute__((always_inline)) {
       for (int jj = j0 - j0 % 3; jj < j1; jj += 3) {
         static_for<0, 3>([&](auto st_c) __attribute__((always_inline)) {
           const int j = jj + decltype(st_c)::value;
-          if (j >= j0 && j < j1) step(st_c, mask_c, ph_c, j);
+          if (j >= j0 && j < j1) step(st_c, mask_c, IC<1>{}, j);
         });
       }
     };
     if (ntl > 0) {
-      if (wl < 0)
-        step(IC<0>{}, std::false_type{}, IC<3>{}, 0);
-      else if (jm > 0)
+      if (jm > 0)
         step(IC<0>{}, std::false_type{}, IC<0>{}, 0);
       else
         step(IC<0>{}, std::true_type{}, IC<0>{}, 0);
-      run(std::false_type{}, IC<1>{}, 1, min(jm, wl + 1));
-      run(std::true_type{}, IC<1>{}, max(jm, 1), wl + 1);
-      if (wl >= 0) {
-        // the PV of tile wl, in slot (wl + 1) % 3 as a compile-time index
-        const int sl = (wl + 1) % 3;
-        if (sl == 0)
-          step(IC<0>{}, std::true_type{}, IC<2>{}, wl + 1);
-        else if (sl == 1)
-          step(IC<1>{}, std::true_type{}, IC<2>{}, wl + 1);
-        else
-          step(IC<2>{}, std::true_type{}, IC<2>{}, wl + 1);
-      }
-      run(std::false_type{}, IC<3>{}, max(wl + 2, 1), ntl + 1);
+      run(std::false_type{}, 1, jm);
+      run(std::true_type{}, max(jm, 1), ntl);
+      // the last step's slot, ntl % 3, as a compile-time index
+      const int sl = ntl % 3;
+      if (sl == 0)
+        step(IC<0>{}, std::true_type{}, IC<2>{}, ntl);
+      else if (sl == 1)
+        step(IC<1>{}, std::true_type{}, IC<2>{}, ntl);
+      else
+        step(IC<2>{}, std::true_type{}, IC<2>{}, ntl);
     }
     if (grp == 0) wg_barrier();
     finish(0);
