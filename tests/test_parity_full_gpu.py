@@ -202,3 +202,37 @@ def test_value_identity_shows_softmax_rows_packed():
     assert err.max() <= O_MAX and err.mean() <= O_MEAN
     assert np.abs(lse.cpu().double().numpy() - lse_r).max() <= LSE_MAX
     assert np.abs(og.sum(axis=-1) - 1.0).max() <= d * 2 ** -8
+
+
+# ------------------------------------------------------------------ late maxima, every schedule
+def _late_maximum_inputs(n, d, dtype, seed):
+    """Q ~ N(0,1) and K = 8 Q: key i is row i's own dominant key, so in key order each row's
+    running maximum stays low until its own key arrives and then jumps by far more than the
+    lazy-rescale margin -- in whatever tile that key falls.  Every speculative step whose test
+    fails there has to fall back to the plain step (in place: from scores formed again)."""
+    q, _, v = inputs.dense_qkv(1, n, n, 2, d, dtype, seed=seed)
+    return q, _dominant_inputs(q, 8.0), v
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_late_maxima_every_config_d128(causal):
+    """Rows whose maximum jumps in a late tile, through every compiled d_head 128 configuration
+    (every schedule, tile width and stage count), against the whole-matrix oracle."""
+    n, d = 1000, 128
+    q, k, v = _late_maximum_inputs(n, d, "bf16", seed=191 + causal)
+    scale = d ** -0.5
+    o_r, lse_r = attn_matmul.attention(inputs.to_f64(q), inputs.to_f64(k), inputs.to_f64(v), scale, causal=causal)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    try:
+        for c in fa.fa_fwd_list_configs(d, fa.FA_BF16):
+            fa.fa_fwd_set_config(d, fa.FA_BF16, c)
+            say("case late maxima causal=%d %r" % (causal, c))
+            o = torch.full_like(qd, float("nan"))
+            lse = torch.full((1, 2, n), float("nan"), device=qd.device)
+            fa.fa_fwd_ext(qd, kd, vd, o, lse, scale=scale, causal=causal, num_splits=1)
+            torch.cuda.synchronize()
+            err = np.abs(inputs.to_f64(o) - o_r)
+            lerr = np.abs(lse.cpu().double().numpy() - lse_r).max()
+            assert err.max() <= O_MAX and err.mean() <= O_MEAN and lerr <= LSE_MAX, (c, err.max(), lerr)
+    finally:
+        fa.fa_fwd_set_config(d, fa.FA_BF16, None)
