@@ -21,7 +21,7 @@
 //    of dQ into an fp32 accumulator in HBM with atomic adds, converted at the end.
 //
 // Kernels:
-//   fa_bwd_pre_kernel      D_i = <dO_i, O_i> (the page's simplification of P_i . dP_i),
+//   fa_bwd_pre_kernel      -D_i, D_i = <dO_i, O_i> (the page's simplification of P_i . dP_i),
 //                          L_i log2(e) for exp2, and (atomic_dq) a zeroed dQ accumulator row;
 //   fa_bwd_kernel          the dK/dV loop (and, with atomic_dq, the atomic dQ adds);
 //   fa_bwd_dq_pass_kernel  the default dQ pass;
@@ -110,7 +110,7 @@ __global__ void __launch_bounds__(256) fa_bwd_pre_kernel(BwdArgs a) {
   for (int off = LPR / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, LPR);
   if (valid && c8 == 0) {
     const int64_t r = ((int64_t)b * a.heads + h) * a.seqlen_q + row;
-    a.dvec[r] = dot;
+    a.dvec[r] = -dot;
     a.lse2[r] = a.lse[r] * 1.4426950408889634f;
   }
 }
@@ -292,22 +292,29 @@ fa_bwd_kernel(BwdArgs a) {
   const auto rk = make_rsrc(kb_, (uint32_t)(nk - 1) * kv_row_bytes + ROWB);
   const auto rv = make_rsrc(vb, (uint32_t)(nk - 1) * kv_row_bytes + ROWB);
 
-  // The K tile to LDS (B operand of dQ, read transposed), swizzled like the forward's tiles.
-  auto load_rows = [&](const __amdgpu_buffer_rsrc_t &rsrc, char *dst, int row0, uint32_t row_bytes, int nch)
-                       __attribute__((always_inline)) {
-    // the lane id is fetched afresh: offsets recomputed per call cost a few VALU, while
+  // Tiles to LDS (Q and dO; with the atomic dQ also the K tile, B operand of dQ read
+  // transposed), swizzled like the forward's tiles.  Piece u (1 KB) of a tile holds rows
+  // RPP u .. RPP u + RPP - 1; lane ln writes row RPP u + ln / CPR, chunk (ln % CPR) XOR
+  // swz(row).  A wavefront loads pieces wave, wave + NW, ...; swz looks only at the low four
+  // bits of the row, the same for all of them (NW RPP is a multiple of 16), so the lane's
+  // part of the global offset is one value and each piece adds a uniform row offset.
+  constexpr int RPP = 1024 / ROWB, CPR = ROWB / 16;
+  static_assert((NW * RPP) % 16 == 0, "one swizzle pattern per wavefront");
+  auto tile_lane_off = [&](uint32_t row_bytes) __attribute__((always_inline)) {
+    // the lane id is fetched afresh: offsets recomputed per step cost a few VALU, while
     // offsets kept live across the step loop get spilled, and a reload waits for every
     // load in flight (the prefetch included)
-    const int ln = fresh_lane_id();
-    for (int u = wave; u < nch; u += NW) {
-      const int pos = u * 1024 + ln * 16;
-      const int r = pos / ROWB;
-      const int cc = ((pos % ROWB) >> 4) ^ swz<D>(r);
-      const uint32_t goff = (uint32_t)(row0 + r) * row_bytes + cc * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void FA_LDS *)(dst + u * 1024), 16, goff, 0, 0, 0);
-    }
+    const uint32_t ln = (uint32_t)fresh_lane_id();
+    const int r = wave * RPP + (int)(ln / CPR);
+    return (ln / CPR) * row_bytes + (uint32_t)(((int)(ln % CPR) ^ swz<D>(r)) * 16);
   };
-  if constexpr (ATOMIC_DQ) load_rows(rk, sk, k0, kv_row_bytes, NCHK);
+  auto load_rows = [&](const __amdgpu_buffer_rsrc_t &rsrc, char *dst, int row0, uint32_t row_bytes, int nch,
+                       uint32_t lane_off) __attribute__((always_inline)) {
+    for (int u = wave; u < nch; u += NW)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void FA_LDS *)(dst + u * 1024), 16,
+                                               (uint32_t)(row0 + u * RPP) * row_bytes + lane_off, 0, 0, 0);
+  };
+  if constexpr (ATOMIC_DQ) load_rows(rk, sk, k0, kv_row_bytes, NCHK, tile_lane_off(kv_row_bytes));
 
   // The wavefront's 32 keys in registers: B operand of S = Q K^T (K) and dP = dO V^T (V).
   const int kw0 = k0 + 32 * wave;
@@ -344,8 +351,9 @@ fa_bwd_kernel(BwdArgs a) {
     const int64_t hoff = (qrow0 * hd + (int64_t)h * D) * 2;
     const auto rq = make_rsrc((const char *)a.q + hoff, (uint32_t)(nq - 1) * q_row_bytes + ROWB);
     const auto rdo = make_rsrc((const char *)a.dout + hoff, (uint32_t)(nq - 1) * q_row_bytes + ROWB);
-    load_rows(rq, st, q0, q_row_bytes, NCHQ);
-    load_rows(rdo, st + QT, q0, q_row_bytes, NCHQ);
+    const uint32_t lo = tile_lane_off(q_row_bytes);
+    load_rows(rq, st, q0, q_row_bytes, NCHQ, lo);
+    load_rows(rdo, st + QT, q0, q_row_bytes, NCHQ, lo);
     const int64_t vrow = ((int64_t)b * a.heads + h) * a.seqlen_q;
     if (wave == 0) {
       const auto rl = make_rsrc(a.lse2 + vrow, (uint32_t)nq * 4);
@@ -385,20 +393,28 @@ fa_bwd_kernel(BwdArgs a) {
       constexpr int qb = decltype(qb_c)::value;
       constexpr int QO = qb * 32 * ROWB;  // this 32-row block of Q (dO at + QT)
       f32x16 S[1], dP[1];
+      // rows of this lane: query q0 + 32 qb + 8 g + 4 hi + r (accumulator register 4 g + r)
+      const int rb = 32 * qb + 4 * (fl >> 5);
+      // dP starts from -D of its rows (the preprocess stores -D), so that the product leaves
+      // dP - D in the accumulator
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 nd = *(const f32x4 *)(sdv + rb + 8 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dP[0][4 * g + r] = nd[r];
+      }
       // (shorter read lookahead than the forward's: two wavefronts per SIMD hide latency and
       // the registers are needed for dK and dV; S and dP back to back, then P and dS, then
       // the two accumulating products: more independent work than forming dP after dV)
       qk_block<D, 32, F16, 2, QO>(sq, S, kreg, ad);
-      qk_block<D, 32, F16, 2, QO + QT>(sq, dP, vreg, ad);
-      // rows of this lane: query q0 + 32 qb + 8 g + 4 hi + r; L log2(e) and D are read from
-      // LDS four rows at a time, and P and dS packed to 16 bits as they are formed
-      const int rb = 32 * qb + 4 * (fl >> 5);
+      qk_block<D, 32, F16, 2, QO + QT, true>(sq, dP, vreg, ad);
+      // L log2(e) is read from LDS four rows at a time, and P and dS packed to 16 bits as
+      // they are formed
       const int kq = my_key - (q0 + rb);  // (causal) masked where kq > 8 g + r
       i32x4 Pp[2], dSp[2];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 l2 = *(const f32x4 *)(sl2 + rb + 8 * g);
-        const f32x4 dd = *(const f32x4 *)(sdv + rb + 8 * g);
         float pv[4], dsv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -408,7 +424,7 @@ fa_bwd_kernel(BwdArgs a) {
           // sequence, whose zero K row would otherwise meet an unbounded P in dS K
           if ((ATOMIC_DQ && my_key >= nk) || (CAUSAL && kq > 8 * g + r)) p = 0.f;
           pv[r] = p;
-          dsv[r] = p * (dP[0][e] - dd[r]);
+          dsv[r] = p * dP[0][e];
         }
         // register e = 4g + r of step s2 = g / 2, dword (g % 2) * 2 + r / 2
         Pp[g >> 1][2 * (g & 1)] = pack2<F16>(pv[0], pv[1]);
@@ -552,26 +568,33 @@ fa_bwd_dq_pass_kernel(BwdArgs a) {
     qreg[t] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
     doreg[t] = __builtin_amdgcn_raw_buffer_load_b128(rdo, off, 0, 0);
   }
-  // L log2(e) and D of this lane's row (rows past nq: 0, their dQ is not stored)
+  // L log2(e) and -D of this lane's row (rows past nq: 0, their dQ is not stored)
   const int64_t vrow = ((int64_t)b * a.heads + h) * a.seqlen_q;
   const auto rl = make_rsrc(a.lse2 + vrow, (uint32_t)nq * 4);
   const auto rd = make_rsrc(a.dvec + vrow, (uint32_t)nq * 4);
   // (the b32 load returns the raw bits as an integer)
   const float l2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)my_row * 4, 0, 0));
-  const float dd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, (uint32_t)my_row * 4, 0, 0));
+  const float nd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, (uint32_t)my_row * 4, 0, 0));
 
-  auto load_one = [&](const __amdgpu_buffer_rsrc_t &rsrc, char *dst, int j) __attribute__((always_inline)) {
-    const uint32_t tile_off = (uint32_t)(j * BC) * kv_row_bytes;
+  // Tile loads, as in the main kernel: piece u (1 KB) holds rows RPP u .., lane ln writes
+  // row RPP u + ln / CPR, chunk (ln % CPR) XOR swz(row); the pieces of a wavefront share the
+  // low four row bits, so the lane's part of the offset is one value (the same for the K
+  // and V tiles, which have the same row pitch).
+  constexpr int RPP = 1024 / ROWB, CPR = ROWB / 16;
+  static_assert(NCH <= NW || (NW * RPP) % 16 == 0, "one swizzle pattern per wavefront");
+  auto tile_lane_off = [&]() __attribute__((always_inline)) {
+    const uint32_t ln = (uint32_t)fresh_lane_id();  // (recomputed per step, not kept live across the loop)
+    const int r = wave * RPP + (int)(ln / CPR);
+    return (ln / CPR) * kv_row_bytes + (uint32_t)(((int)(ln % CPR) ^ swz<D>(r)) * 16);
+  };
+  auto load_one = [&](const __amdgpu_buffer_rsrc_t &rsrc, char *dst, int j, uint32_t lane_off)
+                      __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < (NCH + NW - 1) / NW; ++i) {
       const int u = wave + i * NW;
-      if (NCH % NW == 0 || u < NCH) {
-        const int pos = u * 1024 + lane * 16;
-        const int r = pos / ROWB;
-        const int cc = ((pos % ROWB) >> 4) ^ swz<D>(r);
-        const uint32_t goff = tile_off + (uint32_t)r * kv_row_bytes + cc * 16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void FA_LDS *)(dst + u * 1024), 16, goff, 0, 0, 0);
-      }
+      if (NCH % NW == 0 || u < NCH)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void FA_LDS *)(dst + u * 1024), 16,
+                                                 (uint32_t)(j * BC + u * RPP) * kv_row_bytes + lane_off, 0, 0, 0);
     }
   };
 
@@ -596,8 +619,9 @@ fa_bwd_dq_pass_kernel(BwdArgs a) {
     wg_barrier();
     if (j + 1 < nkt) {
       constexpr int NS = ST ^ 1;
-      load_one(rk, smem + NS * STAGE, j + 1);
-      load_one(rv, smem + NS * STAGE + TILE, j + 1);
+      const uint32_t lo = tile_lane_off();
+      load_one(rk, smem + NS * STAGE, j + 1, lo);
+      load_one(rv, smem + NS * STAGE + TILE, j + 1, lo);
     }
     if (!MK || j * BC < wave_kend) {
       f32x16 S[KB], dP[KB];
@@ -613,7 +637,7 @@ fa_bwd_dq_pass_kernel(BwdArgs a) {
         for (int r = 0; r < 16; ++r) {
           float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], c, -l2));
           if (MK && j * BC + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3) >= klim) p = 0.f;
-          dsv[r] = p * (dP[kb][r] - dd);
+          dsv[r] = p * (dP[kb][r] + nd);
         }
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
@@ -624,8 +648,9 @@ fa_bwd_dq_pass_kernel(BwdArgs a) {
     }
   };
   if (nkt > 0) {
-    load_one(rk, smem, 0);
-    load_one(rv, smem + TILE, 0);
+    const uint32_t lo = tile_lane_off();
+    load_one(rk, smem, 0, lo);
+    load_one(rv, smem + TILE, 0, lo);
   }
   // Tiles [0, jm) need no mask and [jm, nkt) may: each range in a loop of its own (with the
   // mask under a branch the compiler copies the scores between registers on every tile).
