@@ -20,8 +20,7 @@ struct BwdArgs {
   float scale_log2;  // scale * log2(e)
   float *dq_acc;     // [rows, heads, D] fp32, rows = batch * seqlen_q (packed: token rows), for
                      // dQ by atomic adds; nullptr = dQ by the separate pass
-  float *dvec;       // [batch, heads, seqlen_q]: -D_i = -<dO_i, O_i> (negated: the main kernel
-                     // starts its dP accumulator from it)
+  float *dvec;       // [batch, heads, seqlen_q]: D_i = <dO_i, O_i>
   float *lse2;       // [batch, heads, seqlen_q]: L_i log2(e)
 };
 

@@ -21,7 +21,7 @@
 //    of dQ into an fp32 accumulator in HBM with atomic adds, converted at the end.
 //
 // Kernels:
-//   fa_bwd_pre_kernel      -D_i, D_i = <dO_i, O_i> (the page's simplification of P_i . dP_i),
+//   fa_bwd_pre_kernel      D_i = <dO_i, O_i> (the page's simplification of P_i . dP_i),
 //                          L_i log2(e) for exp2, and (atomic_dq) a zeroed dQ accumulator row;
 //   fa_bwd_kernel          the dK/dV loop (and, with atomic_dq, the atomic dQ adds);
 //   fa_bwd_dq_pass_kernel  the default dQ pass;
@@ -110,7 +110,7 @@ __global__ void __launch_bounds__(256) fa_bwd_pre_kernel(BwdArgs a) {
   for (int off = LPR / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, LPR);
   if (valid && c8 == 0) {
     const int64_t r = ((int64_t)b * a.heads + h) * a.seqlen_q + row;
-    a.dvec[r] = -dot;
+    a.dvec[r] = dot;
     a.lse2[r] = a.lse[r] * 1.4426950408889634f;
   }
 }
@@ -393,28 +393,20 @@ fa_bwd_kernel(BwdArgs a) {
       constexpr int qb = decltype(qb_c)::value;
       constexpr int QO = qb * 32 * ROWB;  // this 32-row block of Q (dO at + QT)
       f32x16 S[1], dP[1];
-      // rows of this lane: query q0 + 32 qb + 8 g + 4 hi + r (accumulator register 4 g + r)
-      const int rb = 32 * qb + 4 * (fl >> 5);
-      // dP starts from -D of its rows (the preprocess stores -D), so that the product leaves
-      // dP - D in the accumulator
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 nd = *(const f32x4 *)(sdv + rb + 8 * g);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dP[0][4 * g + r] = nd[r];
-      }
       // (shorter read lookahead than the forward's: two wavefronts per SIMD hide latency and
       // the registers are needed for dK and dV; S and dP back to back, then P and dS, then
       // the two accumulating products: more independent work than forming dP after dV)
       qk_block<D, 32, F16, 2, QO>(sq, S, kreg, ad);
-      qk_block<D, 32, F16, 2, QO + QT, true>(sq, dP, vreg, ad);
-      // L log2(e) is read from LDS four rows at a time, and P and dS packed to 16 bits as
-      // they are formed
+      qk_block<D, 32, F16, 2, QO + QT>(sq, dP, vreg, ad);
+      // rows of this lane: query q0 + 32 qb + 8 g + 4 hi + r; L log2(e) and D are read from
+      // LDS four rows at a time, and P and dS packed to 16 bits as they are formed
+      const int rb = 32 * qb + 4 * (fl >> 5);
       const int kq = my_key - (q0 + rb);  // (causal) masked where kq > 8 g + r
       i32x4 Pp[2], dSp[2];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 l2 = *(const f32x4 *)(sl2 + rb + 8 * g);
+        const f32x4 dd = *(const f32x4 *)(sdv + rb + 8 * g);
         float pv[4], dsv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -424,7 +416,7 @@ fa_bwd_kernel(BwdArgs a) {
           // sequence, whose zero K row would otherwise meet an unbounded P in dS K
           if ((ATOMIC_DQ && my_key >= nk) || (CAUSAL && kq > 8 * g + r)) p = 0.f;
           pv[r] = p;
-          dsv[r] = p * dP[0][e];
+          dsv[r] = p * (dP[0][e] - dd[r]);
         }
         // register e = 4g + r of step s2 = g / 2, dword (g % 2) * 2 + r / 2
         Pp[g >> 1][2 * (g & 1)] = pack2<F16>(pv[0], pv[1]);
@@ -568,13 +560,13 @@ fa_bwd_dq_pass_kernel(BwdArgs a) {
     qreg[t] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
     doreg[t] = __builtin_amdgcn_raw_buffer_load_b128(rdo, off, 0, 0);
   }
-  // L log2(e) and -D of this lane's row (rows past nq: 0, their dQ is not stored)
+  // L log2(e) and D of this lane's row (rows past nq: 0, their dQ is not stored)
   const int64_t vrow = ((int64_t)b * a.heads + h) * a.seqlen_q;
   const auto rl = make_rsrc(a.lse2 + vrow, (uint32_t)nq * 4);
   const auto rd = make_rsrc(a.dvec + vrow, (uint32_t)nq * 4);
   // (the b32 load returns the raw bits as an integer)
   const float l2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)my_row * 4, 0, 0));
-  const float nd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, (uint32_t)my_row * 4, 0, 0));
+  const float dd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, (uint32_t)my_row * 4, 0, 0));
 
   // Tile loads, as in the main kernel: piece u (1 KB) holds rows RPP u .., lane ln writes
   // row RPP u + ln / CPR, chunk (ln % CPR) XOR swz(row); the pieces of a wavefront share the
@@ -637,7 +629,7 @@ fa_bwd_dq_pass_kernel(BwdArgs a) {
         for (int r = 0; r < 16; ++r) {
           float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][r], c, -l2));
           if (MK && j * BC + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3) >= klim) p = 0.f;
-          dsv[r] = p * (dP[kb][r] + nd);
+          dsv[r] = p * (dP[kb][r] - dd);
         }
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)

@@ -244,9 +244,8 @@ using IC = std::integral_constant<int, V>;
 // S^T = K_tile Q^T for one 32-query block: KB accumulators of 32 keys x 32 queries.  MFMA i
 // (t = i / KB, kb = i % KB) reads its K operand LA reads ahead.
 // SOFF is a byte offset from sk carried in the reads' immediate field, so that the per-lane
-// addresses (one register per d step) do not depend on which ring slot is read.  With ACC the
-// products are added to S as it comes in; otherwise S starts from zero.
-template <int D, int BC, bool F16, int LA = 6, int SOFF = 0, bool ACC = false>
+// addresses (one register per d step) do not depend on which ring slot is read.
+template <int D, int BC, bool F16, int LA = 6, int SOFF = 0>
 __device__ __forceinline__ void qk_block(const char *sk, f32x16 (&S)[BC / 32], const i32x4 (&qr)[D / 16],
                                          const LdsAddr &ad) {
   constexpr int ROWB = D * 2, KB = BC / 32, T = D / 16, N = T * KB;
@@ -256,10 +255,8 @@ __device__ __forceinline__ void qk_block(const char *sk, f32x16 (&S)[BC / 32], c
   uint32_t koff[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) koff[t] = sk_lds + (uint32_t)(((32 * t) ^ ad.kx) + ad.kbase);
-  if constexpr (!ACC) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) S[kb] = f32x16{};
-  }
+  for (int kb = 0; kb < KB; ++kb) S[kb] = f32x16{};
   i32x4 buf[L + 1];
   auto issue = [&buf, &koff](auto i_c) __attribute__((always_inline)) {
     constexpr int i = decltype(i_c)::value;
