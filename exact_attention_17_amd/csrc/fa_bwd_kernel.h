@@ -574,11 +574,9 @@ fa_bwd_dq_pass_kernel(BwdArgs a) {
   // and V tiles, which have the same row pitch).
   constexpr int RPP = 1024 / ROWB, CPR = ROWB / 16;
   static_assert(NCH <= NW || (NW * RPP) % 16 == 0, "one swizzle pattern per wavefront");
-  auto tile_lane_off = [&]() __attribute__((always_inline)) {
-    const uint32_t ln = (uint32_t)fresh_lane_id();  // (recomputed per step, not kept live across the loop)
-    const int r = wave * RPP + (int)(ln / CPR);
-    return (ln / CPR) * kv_row_bytes + (uint32_t)(((int)(ln % CPR) ^ swz<D>(r)) * 16);
-  };
+  // (one register, formed once: this pass has registers to spare)
+  const uint32_t tile_lane_off = ((uint32_t)lane / CPR) * kv_row_bytes +
+                                 (uint32_t)(((lane % CPR) ^ swz<D>(wave * RPP + lane / CPR)) * 16);
   auto load_one = [&](const __amdgpu_buffer_rsrc_t &rsrc, char *dst, int j, uint32_t lane_off)
                       __attribute__((always_inline)) {
 #pragma unroll
@@ -611,9 +609,8 @@ fa_bwd_dq_pass_kernel(BwdArgs a) {
     wg_barrier();
     if (j + 1 < nkt) {
       constexpr int NS = ST ^ 1;
-      const uint32_t lo = tile_lane_off();
-      load_one(rk, smem + NS * STAGE, j + 1, lo);
-      load_one(rv, smem + NS * STAGE + TILE, j + 1, lo);
+      load_one(rk, smem + NS * STAGE, j + 1, tile_lane_off);
+      load_one(rv, smem + NS * STAGE + TILE, j + 1, tile_lane_off);
     }
     if (!MK || j * BC < wave_kend) {
       f32x16 S[KB], dP[KB];
@@ -640,9 +637,8 @@ fa_bwd_dq_pass_kernel(BwdArgs a) {
     }
   };
   if (nkt > 0) {
-    const uint32_t lo = tile_lane_off();
-    load_one(rk, smem, 0, lo);
-    load_one(rv, smem + TILE, 0, lo);
+    load_one(rk, smem, 0, tile_lane_off);
+    load_one(rv, smem + TILE, 0, tile_lane_off);
   }
   // Tiles [0, jm) need no mask and [jm, nkt) may: each range in a loop of its own (with the
   // mask under a branch the compiler copies the scores between registers on every tile).
