@@ -132,14 +132,19 @@ def test_bwd_longer_sequence():
 
 
 # ------------------------------------------------------------------------------ full size
-def _sampled_rows(rng, n_rows, heads, n, extra):
-    return sorted(set([(int(rng.integers(heads)), int(rng.integers(n_rows))) for _ in range(n)] + extra))
+def _one_per_block(rng, n, block=32):
+    """One row in each block of 32 rows (the rows a wavefront owns in both backward kernels),
+    at a seeded offset, and the last row."""
+    rows = [min(n - 1, b0 + int(rng.integers(block))) for b0 in range(0, n, block)]
+    return sorted(set(rows + [n - 1]))
 
 
 @pytest.mark.parametrize("name", ["full", "causal", "gqa", "varlen"])
-def test_bwd_full_size_sampled_rows(name):
-    """The named workload at full size, as the benchmark runs it: dQ on sampled query rows and
-    dK, dV on sampled key rows of two sequences, against the oracle's selected-rows backward."""
+def test_bwd_full_size_every_wavefront(name):
+    """The named workload at full size, as the benchmark runs it, with dQ, dK and dV prefilled
+    with NaN: every element must be written and finite, and in every sequence one row of every
+    32-row block of every head (so of every wavefront of every workgroup of the dQ pass and of
+    the dK/dV kernel) is compared with the oracle's selected-rows backward."""
     w = inputs.workload(name)
     dev = torch.device("cuda:0")
     say("case bwd full size %s" % name)
@@ -149,30 +154,29 @@ def test_bwd_full_size_sampled_rows(name):
     o, lse = fa.fa_fwd_ext(qd, kd, vd, scale=w["scale"], causal=w["causal"], cu_seqlens=cud,
                            max_seqlen=w["max_seqlen"])
     do = dout_like(w["q"], w["seed"] + 1000)
-    dq, dk, dv = fa.fa_bwd(qd, kd, vd, o, lse, do.to(dev), scale=w["scale"], causal=w["causal"], cu_seqlens=cud,
-                           max_seqlen=w["max_seqlen"])
+    dq = torch.full_like(qd, float("nan"))
+    dk = torch.full_like(kd, float("nan"))
+    dv = torch.full_like(vd, float("nan"))
+    fa.fa_bwd(qd, kd, vd, o, lse, do.to(dev), dq, dk, dv, scale=w["scale"], causal=w["causal"], cu_seqlens=cud,
+              max_seqlen=w["max_seqlen"])
     torch.cuda.synchronize()
+    for key, t in (("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert bool(torch.isfinite(t).all()), (name, key, "unwritten or non-finite elements")
     rng = np.random.default_rng(len(name) + 7)
     heads, hkv = w["heads"], w["heads_kv"]
     errs = {"dQ": [], "dK": [], "dV": []}
     refs = {"dQ": [], "dK": [], "dV": []}
-    seqs = [0, w["batch"] - 1]
-    for b in seqs:
+    for b in range(w["batch"]):
         if cu is None:
-            sl = (slice(b, b + 1),)
             n = w["seqlen_q"]
             take = lambda t: t[b]  # noqa: E731
         else:
             s0, s1 = int(cu[b]), int(cu[b + 1])
             n = s1 - s0
             take = lambda t, s0=s0, s1=s1: t[s0:s1]  # noqa: E731
-        qrows = _sampled_rows(rng, n, heads, 24, [(0, 0), (heads - 1, n - 1)])
-        krows = sorted(set((hk, j) for hk in (0, hkv - 1)
-                           for j in [0, n - 1] + [int(x) for x in rng.integers(n, size=10)]))
-        if cu is None:
-            qb, kb, vb, db = (inputs.to_f64(t[b:b + 1]) for t in (w["q"], w["k"], w["v"], do))
-        else:
-            qb, kb, vb, db = (inputs.to_f64(take(t)[None]) for t in (w["q"], w["k"], w["v"], do))
+        qrows = [(h, i) for h in range(heads) for i in _one_per_block(rng, n)]
+        krows = [(hk, j) for hk in range(hkv) for j in _one_per_block(rng, n)]
+        qb, kb, vb, db = (inputs.to_f64(take(t)[None]) for t in (w["q"], w["k"], w["v"], do))
         rq, rk, rv = oracle.attention_bwd_rows(qb, kb, vb, db, w["scale"], [(0, h, i) for h, i in qrows],
                                                [(0, hk, j) for hk, j in krows], causal=w["causal"])
         gq = take(dq)[[i for _, i in qrows], [h for h, _ in qrows]].cpu().to(torch.float64).numpy()
@@ -181,10 +185,11 @@ def test_bwd_full_size_sampled_rows(name):
         for key, g, r in (("dQ", gq, rq), ("dK", gk, rk), ("dV", gv, rv)):
             errs[key].append(np.abs(g - r).ravel())
             refs[key].append(np.abs(r).ravel())
+        say("  %s sequence %d of %d compared" % (name, b + 1, w["batch"]))
     bad = []
     for key in ("dQ", "dK", "dV"):
         err, ref = np.concatenate(errs[key]), np.concatenate(refs[key])
-        say("%s %s (%d sampled values): max err %.3g (ref max %.3g)  mean err %.3g (ref mean %.3g)"
+        say("%s %s (%d compared values): max err %.3g (ref max %.3g)  mean err %.3g (ref mean %.3g)"
             % (name, key, err.size, err.max(), ref.max(), err.mean(), ref.mean()))
         if not (err.max() <= REL_MAX * ref.max() + ABS_MAX and err.mean() <= REL_MEAN * ref.mean() + ABS_MEAN):
             bad.append(key)
