@@ -673,9 +673,11 @@ hipError_t launch_fa_bwd(const BwdArgs &a, hipStream_t stream) {
     return hipLaunchKernel((const void *)&fa_bwd_dq_kernel<D, F16>, dim3(bh * ((a.seqlen_q + RPB_DQ - 1) / RPB_DQ)),
                            dim3(256), args, 0, stream);
   } else {
-    // eight wavefronts (256 query rows) at d_head 128 with 32-key tiles, which keeps the
-    // pass within 256 registers per lane (two wavefronts per SIMD) without spilling
-    constexpr int NWQ = D == 128 ? 8 : 4;
+    // four wavefronts (128 query rows) per workgroup, two workgroups per CU, whose steps are
+    // not tied together by barriers (one eight-wavefront workgroup was 2.7 % slower under the
+    // causal mask, the same otherwise); 32-key tiles at d_head 128 keep the pass within 256
+    // registers per lane (two wavefronts per SIMD) without spilling
+    constexpr int NWQ = 4;
     constexpr int BCQ = D == 128 ? 32 : 64;
     constexpr int BRQ = 32 * NWQ;
     return hipLaunchKernel(a.causal ? (const void *)&fa_bwd_dq_pass_kernel<D, BCQ, NWQ, F16, true>
