@@ -262,9 +262,24 @@ fa_bwd_kernel(BwdArgs a) {
   const int G = a.total_wgs;
   const int per = G >> 3, rem = G & 7, xcd = w & 7;
   const int lin = xcd * per + min(xcd, rem) + (w >> 3);
-  // head-major, as in the forward: every XCD gets a share of every (packed) sequence
-  const int kt = lin % a.n_ktiles;
-  const int hkb = lin / a.n_ktiles;
+  // head-major, as in the forward: every XCD gets a share of every (packed) sequence, and
+  // the workgroups of one (sequence, K/V head), which stream the same Q and dO tiles, run
+  // together on one XCD.  Under the causal mask the work of a key tile falls with its index;
+  // there, within windows of kCausalWindow consecutive (sequence, K/V head) groups, the
+  // workgroups go out key tile by key tile (longest first), which evens out the CUs' ends
+  // while the window's Q/dO streams still fit the XCD's L2 (windows of 4-8 groups: 2.5-6 %
+  // faster; 32: 2 % slower; all groups: 36 % slower).
+  constexpr int kCausalWindow = 8;
+  int kt = lin % a.n_ktiles;
+  int hkb = lin / a.n_ktiles;
+  if (CAUSAL) {
+    const int ng = a.total_wgs / a.n_ktiles;  // (sequence, K/V head) groups
+    const int g0 = hkb - hkb % kCausalWindow;
+    const int wg = min(kCausalWindow, ng - g0);
+    const int o = lin - g0 * a.n_ktiles;
+    kt = o / wg;
+    hkb = g0 + o % wg;
+  }
   const int b = hkb % a.batch;
   const int hk = hkb / a.batch;
 
